@@ -1,0 +1,204 @@
+/*
+ * pkv.h -- C ABI of libpkv: the Qwen3 attention-sublayer core on MI355X (gfx950).
+ *
+ * The library runs four steps of one attention sublayer, each on the caller's
+ * HIP stream, in the order the attention pages describe them:
+ *
+ *   pkv_qk_norm_rope         per-head RMSNorm of q and k, then RoPE
+ *   pkv_store_kvcache        scatter of k and v rows into the paged KV cache
+ *   pkv_attn_prefill_varlen  varlen causal GQA prefill (fresh K/V or paged)
+ *   pkv_attn_decode_paged    single-token paged decode
+ *
+ * plus pkv_rope_cache_build, which fills the cos/sin table once at set-up.
+ *
+ * Conventions for every entry point
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, unless
+ *     stated otherwise.  The library keeps no pointer after a call returns.
+ *   - bf16 tensors are passed as raw 16-bit patterns (void*).  Integer
+ *     metadata is int32 except positions (int64).
+ *   - Row strides are counted in ELEMENTS, not bytes.  Inside a row, heads
+ *     are contiguous blocks of head_dim elements and head_dim elements are
+ *     contiguous (the pages' stride(-1) == 1, stride(1) == head_dim).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *     enqueued asynchronously; no entry point synchronises, allocates or
+ *     frees device memory.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid argument returns a negative status and nothing is launched.
+ *     pkv_last_error() then returns a thread-local message.
+ *   - Contents of device arrays (slot ids, block ids, lengths) cannot be
+ *     checked on the host.  Kernels never access memory outside the buffers
+ *     the sizes describe: a slot outside [0, num_slots) is not written, a
+ *     block id outside [0, num_blocks) is not read and the key it would hold
+ *     is dropped from the softmax.  Results for rows whose metadata is
+ *     invalid are unspecified.
+ *   - Only head_dim == 128 and block_size == 256 are built (Qwen3 shapes);
+ *     other values return PKV_ERR_UNSUPPORTED.
+ *
+ * Citations name the page and section that defines each operation:
+ *   "3.3 Model skeleton and core operators" (infra-guide)        = [Ops]
+ *   "Nano-vLLM 源码解读 #17 注意力层" (yeyulingfeng)             = [Attn17]
+ *   "同一个 Qwen3，两种写法" (violet-quartz)                      = [TwoWays]
+ *   "nano-vllm code walkthrough" (roba269)                        = [Walk]
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef PKV_API
+#define PKV_API __attribute__((visibility("default")))
+#endif
+
+typedef enum {
+    PKV_OK = 0,
+    PKV_ERR_INVALID_ARG = -1,  /* null pointer, bad size or stride, Hq % Hkv != 0, ... */
+    PKV_ERR_UNSUPPORTED = -2,  /* head_dim != 128, block_size != 256, causal == 0, ... */
+    PKV_ERR_LAUNCH = -3,       /* the HIP runtime refused a launch */
+    PKV_ERR_WORKSPACE = -4     /* decode workspace missing or too small */
+} pkv_status;
+
+/* Message describing the last failure on the calling thread ("" if none).
+ * The string stays valid until the next pkv_* call on the same thread. */
+PKV_API const char* pkv_last_error(void);
+
+/* Library version, (major << 16) | minor. */
+PKV_API int pkv_version(void);
+
+/*
+ * pkv_rope_cache_build -- cos/sin table for RoPE, [Ops] s3; [TwoWays] s3.5.
+ *
+ *   cos_sin_cache  device fp32 [max_position][rotary_dim], written entirely.
+ *                  Row p = [cos(p f_0) .. cos(p f_{r/2-1}) | sin(p f_0) .. sin(p f_{r/2-1})]
+ *                  with f_i = fp32(theta^(-2i/rotary_dim)); the angle is the fp32
+ *                  product fp32(p) * f_i and cos/sin of it are rounded to fp32.
+ *   max_position   number of rows (the pages use 40960), > 0.
+ *   rotary_dim     must equal head_dim (the pages assert rotary_dim == head_size): 128.
+ *   theta          rope_theta (1e6 for Qwen3), > 0.
+ * One table serves every layer; build it once and keep it.
+ */
+PKV_API int pkv_rope_cache_build(float* cos_sin_cache, int32_t max_position, int32_t rotary_dim, double theta,
+                         void* stream);
+
+/*
+ * pkv_qk_norm_rope -- QK-Norm then RoPE on q and k, [Ops] s2, s3, s8;
+ * [Attn17] s4.  For every token t and head h of q (and of k):
+ *     r   = 1 / sqrt(mean_i x_i^2 + eps)
+ *     y_i = x_i * r * gamma_i                    (gamma = q_norm / k_norm weight)
+ *     (c, s) = cos_sin_cache[positions[t]] halves
+ *     out[i]      = y_i * c_i - y_{i+64} * s_i
+ *     out[i + 64] = y_{i+64} * c_i + y_i * s_i    (i < 64)
+ * computed in fp32 and rounded once to bf16 (round to nearest even).
+ *
+ *   q, q_row_stride     bf16 rows of num_q_heads*head_dim elements (e.g. the q
+ *                       columns of the fused qkv rows: stride = qkv width).
+ *   k, k_row_stride     bf16 rows of num_kv_heads*head_dim elements.
+ *   q_out, k_out        bf16, contiguous [n_tokens][heads][head_dim].  They may
+ *                       alias q / k exactly (in place) when the strides equal
+ *                       the contiguous row length; partial overlap is invalid.
+ *   positions           int64 [n_tokens]; each in [0, max_position) (positions
+ *                       outside are clamped to the table range).
+ *   q_norm_weight, k_norm_weight   bf16 [head_dim].
+ *   cos_sin_cache       fp32 [max_position][head_dim] from pkv_rope_cache_build.
+ * n_tokens == 0 is valid and launches nothing.  V is not touched ([Ops] s3).
+ */
+PKV_API int pkv_qk_norm_rope(const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride, void* q_out,
+                     void* k_out, const int64_t* positions, int32_t n_tokens, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, const void* q_norm_weight, const void* k_norm_weight,
+                     float eps, const float* cos_sin_cache, int32_t max_position, void* stream);
+
+/*
+ * pkv_store_kvcache -- scatter of this step's K/V rows into the paged cache,
+ * [Ops] s7.1; [Attn17] s5.1.  For each token t with s = slot_mapping[t]:
+ *     s == -1           -> nothing is written (padding rows)
+ *     0 <= s < num_slots -> k_cache row s = key row t, v_cache row s = value row t
+ * A row is D = num_kv_heads * head_dim elements of elem_bytes bytes, copied
+ * bit for bit.  The caches are [num_blocks][block_size][num_kv_heads][head_dim]
+ * viewed as num_slots = num_blocks * block_size contiguous rows of D elements
+ * (the pages' k_cache.stride(1) == D).  Duplicate slots within one call are
+ * invalid input: which row lands is unspecified.
+ *
+ *   key, key_row_stride       rows of D elements, key_row_stride >= D.
+ *   value, value_row_stride   rows of D elements (e.g. the v columns of qkv).
+ *   slot_mapping              int32 [n_tokens].
+ *   elem_bytes                2 for bf16 (any of 1, 2, 4 is accepted).
+ */
+PKV_API int pkv_store_kvcache(const void* key, int64_t key_row_stride, const void* value, int64_t value_row_stride,
+                      void* k_cache, void* v_cache, int64_t num_slots, const int32_t* slot_mapping,
+                      int32_t n_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t elem_bytes, void* stream);
+
+/*
+ * pkv_attn_prefill_varlen -- causal GQA attention over a packed batch of
+ * variable-length sequences, [Ops] s7.2; [TwoWays] s3.2, s3.4; [Walk]
+ * "Prefill stage".  Sequence b owns query rows cu_seqlens_q[b] ..
+ * cu_seqlens_q[b+1]-1 (Lq_b of them) and Lk_b = cu_seqlens_k[b+1]-cu_seqlens_k[b]
+ * >= Lq_b keys.  Query i of sequence b sits at absolute position Lk_b - Lq_b + i
+ * and attends keys 0 .. Lk_b - Lq_b + i:
+ *     o[t][h] = sum_j softmax_j(softmax_scale * q[t][h] . k_j) v_j
+ * with q head h reading kv head h / (num_q_heads / num_kv_heads).
+ *
+ *   block_table == NULL ("case 1", fresh K/V): key j of sequence b is row
+ *       cu_seqlens_k[b] + j of k / v (row strides k_row_stride / v_row_stride).
+ *   block_table != NULL ("case 2", prefix hit or later chunk): k and v are the
+ *       caches [num_blocks][block_size][num_kv_heads][head_dim]; key j of
+ *       sequence b is cache row block_table[b][j / block_size] * block_size
+ *       + j % block_size.  The row strides must be num_kv_heads*head_dim.
+ *       num_blocks bounds the ids read (ids outside are never dereferenced).
+ *   q, q_row_stride   bf16 rows of num_q_heads*head_dim elements.
+ *   o                 bf16 contiguous [Tq][num_q_heads][head_dim], Tq = cu_seqlens_q[num_seqs].
+ *   cu_seqlens_q/k    int32 [num_seqs+1], non-decreasing, starting at 0.
+ *   max_seqlen_q      >= every Lq_b (sizes the launch grid); max_seqlen_k >= every Lk_b.
+ *   total_q           cu_seqlens_q[num_seqs] (host copy, bounds the q/o rows touched).
+ *   causal            must be 1 (the pages only use causal attention).
+ * Sequences with Lq_b == 0 contribute nothing.  Output rows are written in
+ * full for every query row.
+ */
+PKV_API int pkv_attn_prefill_varlen(const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride,
+                            const void* v, int64_t v_row_stride, void* o, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            float softmax_scale, int32_t causal, const int32_t* block_table,
+                            int32_t max_blocks_per_seq, int32_t block_size, int64_t num_blocks, void* stream);
+
+/*
+ * pkv_attn_decode_workspace_bytes -- device workspace pkv_attn_decode_paged
+ * needs for these sizes (0 on invalid sizes).  Host-only, no HIP call.
+ */
+PKV_API size_t pkv_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size);
+
+/*
+ * pkv_attn_decode_paged -- one new query per sequence against its paged KV,
+ * [Ops] s7.2; [Walk] "Decode Stage"; [Attn17] s5.3.  Sequence b attends its
+ * first context_lens[b] cached keys (the token written this step included):
+ *     o[b][h] = sum_{j < ctx_b} softmax_j(softmax_scale * q[b][h] . k_j) v_j
+ * key j at cache row block_table[b][j / block_size] * block_size + j % block_size,
+ * q head h reading kv head h / (num_q_heads / num_kv_heads).  context_lens[b] == 0
+ * gives a zero output row (padded rows of a fixed-size batch).
+ *
+ *   q                 bf16 contiguous [num_seqs][num_q_heads][head_dim].
+ *   k_cache, v_cache  bf16 [num_blocks][block_size][num_kv_heads][head_dim].
+ *   o                 bf16 contiguous [num_seqs][num_q_heads][head_dim].
+ *   context_lens      int32 [num_seqs], each <= max_blocks_per_seq * block_size.
+ *   block_table       int32 [num_seqs][max_blocks_per_seq], -1 padded.
+ *   workspace         device scratch of at least
+ *                     pkv_attn_decode_workspace_bytes(...) bytes, 256-byte aligned;
+ *                     owned by the caller, contents need no initialisation.
+ * The split of each context into chunks and their merge are deterministic:
+ * the result does not depend on where the blocks sit in the pool.
+ */
+PKV_API int pkv_attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, void* o,
+                          const int32_t* context_lens, const int32_t* block_table, int32_t max_blocks_per_seq,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int64_t num_blocks, float softmax_scale, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -1,0 +1,245 @@
+"""paged_kv_gqa_amd -- the Qwen3 attention-sublayer core on MI355X (gfx950).
+
+A thin ctypes binding over ``libpkv.so`` (HIP kernels + C ABI declared in
+``include/pkv.h``).  The functions below only marshal torch tensors into
+pointers, strides and sizes; every step runs in the HIP kernels.  There is no
+fallback: if the library is missing or cannot be loaded, every call raises.
+
+Entry points mirror the calls the attention pages describe
+("3.3 Model skeleton and core operators", sections 3, 7.1, 7.2, 8):
+
+* ``rope_cache_build``   -- the fp32 cos/sin table, once
+* ``qk_norm_rope``       -- q_norm / k_norm then rotary_emb(positions, q, k)
+* ``store_kvcache``      -- store_kvcache(key, value, k_cache, v_cache, slot_mapping)
+* ``attn_prefill_varlen``-- flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k,
+                            max_seqlen_q, max_seqlen_k, softmax_scale, causal, block_table)
+* ``attn_decode_paged``  -- flash_attn_with_kvcache(q, k_cache, v_cache, cache_seqlens,
+                            block_table, softmax_scale, causal)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpkv.so")
+HEAD_DIM = 128
+BLOCK_SIZE = 256
+
+PKV_OK = 0
+_STATUS = {-1: "invalid argument", -2: "unsupported", -3: "launch failed", -4: "workspace"}
+
+#: every symbol include/pkv.h declares
+EXPORTED = ("pkv_last_error", "pkv_version", "pkv_rope_cache_build", "pkv_qk_norm_rope", "pkv_store_kvcache",
+            "pkv_attn_prefill_varlen", "pkv_attn_decode_workspace_bytes", "pkv_attn_decode_paged")
+
+_lib = None
+
+
+class PkvError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed ({code}: {_STATUS.get(code, '?')}): {msg}")
+        self.code = code
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libpkv.so and declare its C signatures.  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m paged_kv_gqa_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, F32, F64, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                 ctypes.c_double, ctypes.c_size_t)
+    lib.pkv_last_error.argtypes = []
+    lib.pkv_last_error.restype = ctypes.c_char_p
+    lib.pkv_version.argtypes = []
+    lib.pkv_version.restype = ctypes.c_int
+    lib.pkv_rope_cache_build.argtypes = [P, I32, I32, F64, P]
+    lib.pkv_rope_cache_build.restype = ctypes.c_int
+    lib.pkv_qk_norm_rope.argtypes = [P, I64, P, I64, P, P, P, I32, I32, I32, I32, P, P, F32, P, I32, P]
+    lib.pkv_qk_norm_rope.restype = ctypes.c_int
+    lib.pkv_store_kvcache.argtypes = [P, I64, P, I64, P, P, I64, P, I32, I32, I32, I32, P]
+    lib.pkv_store_kvcache.restype = ctypes.c_int
+    lib.pkv_attn_prefill_varlen.argtypes = [P, I64, P, I64, P, I64, P, P, P, I32, I32, I32, I32, I32, I32, I32,
+                                            F32, I32, P, I32, I32, I64, P]
+    lib.pkv_attn_prefill_varlen.restype = ctypes.c_int
+    lib.pkv_attn_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
+    lib.pkv_attn_decode_workspace_bytes.restype = SZ
+    lib.pkv_attn_decode_paged.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I64, F32, P, SZ, P]
+    lib.pkv_attn_decode_paged.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, rc: int):
+    if rc != PKV_OK:
+        raise PkvError(fn, rc, _lib.pkv_last_error().decode(errors="replace"))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _rows(x, heads: int, name: str) -> int:
+    """Validate a [N, heads, 128] bf16 view (the pages' stride asserts) and return its row stride."""
+    import torch
+    if x.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {x.dtype}")
+    if x.dim() != 3 or x.shape[1] != heads or x.shape[2] != HEAD_DIM:
+        raise ValueError(f"{name} must be [N, {heads}, {HEAD_DIM}], got {tuple(x.shape)}")
+    if x.shape[0] > 1 and (x.stride(2) != 1 or x.stride(1) != HEAD_DIM):
+        raise ValueError(f"{name} needs stride(-1) == 1 and stride(1) == head_dim, got {x.stride()}")
+    if x.shape[0] <= 1:
+        return max(x.stride(0), heads * HEAD_DIM)
+    return x.stride(0)
+
+
+def _i32(t, name):
+    import torch
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous int32 tensor")
+    return t
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def rope_cache_build(max_position: int = 40960, rotary_dim: int = HEAD_DIM, theta: float = 1.0e6,
+                     device="cuda", stream=None, out=None):
+    """cos/sin table [max_position, rotary_dim] fp32 on the GPU (built by a HIP kernel)."""
+    import torch
+    lib = load_library()
+    if out is None:
+        out = torch.empty((max_position, rotary_dim), dtype=torch.float32, device=device)
+    _check("pkv_rope_cache_build",
+           lib.pkv_rope_cache_build(_ptr(out), max_position, rotary_dim, float(theta), _stream(stream)))
+    return out
+
+
+def qk_norm_rope(q, k, positions, q_norm_weight, k_norm_weight, cos_sin_cache, eps: float = 1.0e-6,
+                 q_out=None, k_out=None, stream=None):
+    """QK-Norm then RoPE.  q: [N, Hq, 128], k: [N, Hkv, 128] bf16 views (row-strided allowed).
+
+    Returns (q_out, k_out), contiguous bf16.  Pass q_out=q / k_out=k to run in place
+    on contiguous inputs.
+    """
+    import torch
+    lib = load_library()
+    n, hq, hkv = q.shape[0], q.shape[1], k.shape[1]
+    qs, ks = _rows(q, hq, "q"), _rows(k, hkv, "k")
+    if k.shape[0] != n or positions.shape[0] != n:
+        raise ValueError("q, k and positions must have the same number of tokens")
+    if positions.dtype != torch.int64 or not positions.is_contiguous():
+        raise TypeError("positions must be a contiguous int64 tensor")
+    if q_out is None:
+        q_out = torch.empty((n, hq, HEAD_DIM), dtype=torch.bfloat16, device=q.device)
+    if k_out is None:
+        k_out = torch.empty((n, hkv, HEAD_DIM), dtype=torch.bfloat16, device=k.device)
+    if not (q_out.is_contiguous() and k_out.is_contiguous()):
+        raise ValueError("q_out and k_out must be contiguous")
+    _check("pkv_qk_norm_rope",
+           lib.pkv_qk_norm_rope(_ptr(q), qs, _ptr(k), ks, _ptr(q_out), _ptr(k_out), _ptr(positions), n, hq, hkv,
+                                HEAD_DIM, _ptr(q_norm_weight), _ptr(k_norm_weight), float(eps),
+                                _ptr(cos_sin_cache), cos_sin_cache.shape[0], _stream(stream)))
+    return q_out, k_out
+
+
+def store_kvcache(key, value, k_cache, v_cache, slot_mapping, stream=None):
+    """Scatter key/value rows [N, Hkv, 128] into the paged caches [num_blocks, 256, Hkv, 128]."""
+    lib = load_library()
+    n, hkv = key.shape[0], key.shape[1]
+    ks, vs = _rows(key, hkv, "key"), _rows(value, hkv, "value")
+    D = hkv * HEAD_DIM
+    if k_cache.stride(1) != D or v_cache.stride(1) != D or not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("caches must be contiguous with stride(1) == num_kv_heads*head_dim")
+    if slot_mapping.numel() != n:
+        raise ValueError("slot_mapping must hold one slot per token")
+    _i32(slot_mapping, "slot_mapping")
+    num_slots = k_cache.numel() // D
+    _check("pkv_store_kvcache",
+           lib.pkv_store_kvcache(_ptr(key), ks, _ptr(value), vs, _ptr(k_cache), _ptr(v_cache), num_slots,
+                                 _ptr(slot_mapping), n, hkv, HEAD_DIM, key.element_size(), _stream(stream)))
+
+
+def attn_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                        softmax_scale: Optional[float] = None, causal: bool = True, block_table=None, out=None,
+                        stream=None):
+    """Varlen causal GQA prefill.  q: [Tq, Hq, 128]; k/v: [Tk, Hkv, 128] (case 1) or the caches
+    [num_blocks, 256, Hkv, 128] with block_table [B, max_blocks] (case 2).  Returns o [Tq, Hq, 128]."""
+    import torch
+    lib = load_library()
+    tq, hq = q.shape[0], q.shape[1]
+    qs = _rows(q, hq, "q")
+    if block_table is not None:
+        if k.dim() != 4 or k.shape[1] != BLOCK_SIZE or not (k.is_contiguous() and v.is_contiguous()):
+            raise ValueError("with block_table, k and v must be contiguous caches [num_blocks, 256, Hkv, 128]")
+        hkv, num_blocks = k.shape[2], k.shape[0]
+        ks = vs = hkv * HEAD_DIM
+        _i32(block_table, "block_table")
+        mb = block_table.shape[1]
+    else:
+        hkv = k.shape[1]
+        ks, vs = _rows(k, hkv, "k"), _rows(v, hkv, "v")
+        num_blocks, mb = 0, 0
+    _i32(cu_seqlens_q, "cu_seqlens_q")
+    _i32(cu_seqlens_k, "cu_seqlens_k")
+    nseq = cu_seqlens_q.numel() - 1
+    scale = HEAD_DIM ** -0.5 if softmax_scale is None else softmax_scale
+    if out is None:
+        out = torch.empty((tq, hq, HEAD_DIM), dtype=torch.bfloat16, device=q.device)
+    _check("pkv_attn_prefill_varlen",
+           lib.pkv_attn_prefill_varlen(_ptr(q), qs, _ptr(k), ks, _ptr(v), vs, _ptr(out), _ptr(cu_seqlens_q),
+                                       _ptr(cu_seqlens_k), nseq, tq, int(max_seqlen_q), int(max_seqlen_k), hq, hkv,
+                                       HEAD_DIM, float(scale), 1 if causal else 0, _ptr(block_table), mb,
+                                       BLOCK_SIZE, num_blocks, _stream(stream)))
+    return out
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, max_blocks_per_seq: int) -> int:
+    lib = load_library()
+    return int(lib.pkv_attn_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, HEAD_DIM,
+                                                   max_blocks_per_seq, BLOCK_SIZE))
+
+
+def attn_decode_paged(q, k_cache, v_cache, cache_seqlens, block_table, softmax_scale: Optional[float] = None,
+                      causal: bool = True, out=None, workspace=None, stream=None):
+    """Paged decode.  q: [B, Hq, 128] (or [B, 1, Hq, 128]); caches [num_blocks, 256, Hkv, 128];
+    cache_seqlens [B] int32 (tokens in cache, the new one included); block_table [B, max_blocks]."""
+    import torch
+    lib = load_library()
+    if q.dim() == 4:
+        if q.shape[1] != 1:
+            raise ValueError("decode takes exactly one query per sequence")
+        q = q[:, 0]
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, Hq, 128]")
+    B, hq = q.shape[0], q.shape[1]
+    _rows(q, hq, "q")
+    if k_cache.dim() != 4 or k_cache.shape[1] != BLOCK_SIZE or not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("caches must be contiguous [num_blocks, 256, Hkv, 128]")
+    hkv, num_blocks = k_cache.shape[2], k_cache.shape[0]
+    _i32(cache_seqlens, "cache_seqlens")
+    _i32(block_table, "block_table")
+    mb = block_table.shape[1]
+    scale = HEAD_DIM ** -0.5 if softmax_scale is None else softmax_scale
+    need = decode_workspace_bytes(B, hq, hkv, mb)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, hq, HEAD_DIM), dtype=torch.bfloat16, device=q.device)
+    _check("pkv_attn_decode_paged",
+           lib.pkv_attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(cache_seqlens),
+                                     _ptr(block_table), mb, B, hq, hkv, HEAD_DIM, BLOCK_SIZE, num_blocks,
+                                     float(scale), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out

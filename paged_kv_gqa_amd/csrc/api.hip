@@ -1,0 +1,246 @@
+// api.hip -- the extern "C" entry points declared in include/pkv.h.
+//
+// Every entry point validates its scalar arguments and pointers on the host,
+// turning the asserts the pages place in front of the store_kvcache kernel
+// ("3.3 Model skeleton and core operators", section 7.1; "Nano-vLLM 源码解读
+// #17 注意力层", section 5.1: contiguous head_dim, contiguous heads, one slot =
+// D contiguous elements, one slot id per token) and the head divisibility the
+// attention layer relies on into status codes, before anything is enqueued.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "pkv.h"
+#include "pkv_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return PKV_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+#define PKV_REQUIRE(cond, code, ...) \
+    do {                             \
+        if (!(cond)) return fail((code), __VA_ARGS__); \
+    } while (0)
+
+int check_heads(const char* fn, int32_t hq, int32_t hkv, int32_t head_dim) {
+    PKV_REQUIRE(hq > 0 && hkv > 0, PKV_ERR_INVALID_ARG, "%s: head counts must be positive (Hq=%d, Hkv=%d)", fn, hq,
+                hkv);
+    PKV_REQUIRE(hq % hkv == 0, PKV_ERR_INVALID_ARG, "%s: num_q_heads %d is not a multiple of num_kv_heads %d", fn, hq,
+                hkv);
+    PKV_REQUIRE(head_dim == 128, PKV_ERR_UNSUPPORTED, "%s: head_dim %d unsupported (only 128)", fn, head_dim);
+    return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_err; }
+
+int pkv_version(void) { return (1 << 16) | 0; }
+
+int pkv_rope_cache_build(float* cos_sin_cache, int32_t max_position, int32_t rotary_dim, double theta,
+                         void* stream) {
+    const char* fn = "pkv_rope_cache_build";
+    PKV_REQUIRE(cos_sin_cache, PKV_ERR_INVALID_ARG, "%s: cos_sin_cache is NULL", fn);
+    PKV_REQUIRE(max_position > 0, PKV_ERR_INVALID_ARG, "%s: max_position must be > 0 (got %d)", fn, max_position);
+    PKV_REQUIRE(rotary_dim == 128, PKV_ERR_UNSUPPORTED, "%s: rotary_dim %d unsupported (only 128 = head_dim)", fn,
+                rotary_dim);
+    PKV_REQUIRE(theta > 0.0, PKV_ERR_INVALID_ARG, "%s: theta must be > 0", fn);
+    return launched(pkv::launch_rope_cache_build(cos_sin_cache, max_position, rotary_dim, theta, (hipStream_t)stream),
+                    fn);
+}
+
+int pkv_qk_norm_rope(const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride, void* q_out,
+                     void* k_out, const int64_t* positions, int32_t n_tokens, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, const void* q_norm_weight, const void* k_norm_weight,
+                     float eps, const float* cos_sin_cache, int32_t max_position, void* stream) {
+    const char* fn = "pkv_qk_norm_rope";
+    int rc = check_heads(fn, num_q_heads, num_kv_heads, head_dim);
+    if (rc) return rc;
+    PKV_REQUIRE(n_tokens >= 0, PKV_ERR_INVALID_ARG, "%s: n_tokens must be >= 0 (got %d)", fn, n_tokens);
+    if (n_tokens == 0) return ok();
+    PKV_REQUIRE(q && k && q_out && k_out && positions && q_norm_weight && k_norm_weight && cos_sin_cache,
+                PKV_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    const int64_t qw = (int64_t)num_q_heads * head_dim, kw = (int64_t)num_kv_heads * head_dim;
+    PKV_REQUIRE(q_row_stride >= qw, PKV_ERR_INVALID_ARG, "%s: q_row_stride %lld < num_q_heads*head_dim %lld", fn,
+                (long long)q_row_stride, (long long)qw);
+    PKV_REQUIRE(k_row_stride >= kw, PKV_ERR_INVALID_ARG, "%s: k_row_stride %lld < num_kv_heads*head_dim %lld", fn,
+                (long long)k_row_stride, (long long)kw);
+    PKV_REQUIRE(q_row_stride % 8 == 0 && k_row_stride % 8 == 0, PKV_ERR_INVALID_ARG,
+                "%s: row strides must be multiples of 8 elements (16-byte rows)", fn);
+    PKV_REQUIRE(((uintptr_t)q | (uintptr_t)k | (uintptr_t)q_out | (uintptr_t)k_out | (uintptr_t)q_norm_weight |
+                 (uintptr_t)k_norm_weight | (uintptr_t)cos_sin_cache) % 16 == 0,
+                PKV_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
+    PKV_REQUIRE(max_position > 0, PKV_ERR_INVALID_ARG, "%s: max_position must be > 0", fn);
+    PKV_REQUIRE(eps >= 0.f, PKV_ERR_INVALID_ARG, "%s: eps must be >= 0", fn);
+    // In place is allowed only as an exact alias of a contiguous input.
+    PKV_REQUIRE(q_out != q || q_row_stride == qw, PKV_ERR_INVALID_ARG,
+                "%s: in-place q needs q_row_stride == num_q_heads*head_dim", fn);
+    PKV_REQUIRE(k_out != k || k_row_stride == kw, PKV_ERR_INVALID_ARG,
+                "%s: in-place k needs k_row_stride == num_kv_heads*head_dim", fn);
+    return launched(pkv::launch_qk_norm_rope(q, q_row_stride, k, k_row_stride, q_out, k_out, positions, n_tokens,
+                                             num_q_heads, num_kv_heads, q_norm_weight, k_norm_weight, eps,
+                                             cos_sin_cache, max_position, (hipStream_t)stream),
+                    fn);
+}
+
+int pkv_store_kvcache(const void* key, int64_t key_row_stride, const void* value, int64_t value_row_stride,
+                      void* k_cache, void* v_cache, int64_t num_slots, const int32_t* slot_mapping,
+                      int32_t n_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t elem_bytes, void* stream) {
+    const char* fn = "pkv_store_kvcache";
+    PKV_REQUIRE(n_tokens >= 0, PKV_ERR_INVALID_ARG, "%s: n_tokens must be >= 0 (got %d)", fn, n_tokens);
+    PKV_REQUIRE(num_kv_heads > 0 && head_dim > 0, PKV_ERR_INVALID_ARG, "%s: num_kv_heads and head_dim must be > 0",
+                fn);
+    PKV_REQUIRE(elem_bytes == 1 || elem_bytes == 2 || elem_bytes == 4, PKV_ERR_INVALID_ARG,
+                "%s: elem_bytes must be 1, 2 or 4 (got %d)", fn, elem_bytes);
+    const int64_t D = (int64_t)num_kv_heads * head_dim;
+    PKV_REQUIRE(key_row_stride >= D && value_row_stride >= D, PKV_ERR_INVALID_ARG,
+                "%s: row strides (%lld, %lld) must be >= D = num_kv_heads*head_dim = %lld", fn,
+                (long long)key_row_stride, (long long)value_row_stride, (long long)D);
+    PKV_REQUIRE(num_slots >= 0, PKV_ERR_INVALID_ARG, "%s: num_slots must be >= 0", fn);
+    if (n_tokens == 0) return ok();
+    PKV_REQUIRE(key && value && k_cache && v_cache && slot_mapping, PKV_ERR_INVALID_ARG,
+                "%s: a required pointer is NULL", fn);
+    PKV_REQUIRE(k_cache != v_cache, PKV_ERR_INVALID_ARG, "%s: k_cache and v_cache must be distinct", fn);
+    return launched(pkv::launch_store_kvcache(key, key_row_stride, value, value_row_stride, k_cache, v_cache,
+                                              num_slots, slot_mapping, n_tokens, D * elem_bytes, elem_bytes,
+                                              (hipStream_t)stream),
+                    fn);
+}
+
+int pkv_attn_prefill_varlen(const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride,
+                            const void* v, int64_t v_row_stride, void* o, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            float softmax_scale, int32_t causal, const int32_t* block_table,
+                            int32_t max_blocks_per_seq, int32_t block_size, int64_t num_blocks, void* stream) {
+    const char* fn = "pkv_attn_prefill_varlen";
+    int rc = check_heads(fn, num_q_heads, num_kv_heads, head_dim);
+    if (rc) return rc;
+    PKV_REQUIRE(causal == 1, PKV_ERR_UNSUPPORTED, "%s: only causal attention is built (causal=%d)", fn, causal);
+    const int G = num_q_heads / num_kv_heads;
+    PKV_REQUIRE(G == 1 || G == 2 || G % 4 == 0, PKV_ERR_UNSUPPORTED,
+                "%s: GQA group %d unsupported (1, 2 or a multiple of 4)", fn, G);
+    PKV_REQUIRE(num_seqs >= 0 && total_q >= 0 && max_seqlen_q >= 0 && max_seqlen_k >= 0, PKV_ERR_INVALID_ARG,
+                "%s: sizes must be >= 0", fn);
+    PKV_REQUIRE(max_seqlen_q <= max_seqlen_k || num_seqs == 0, PKV_ERR_INVALID_ARG,
+                "%s: max_seqlen_q %d > max_seqlen_k %d (every sequence needs Lk >= Lq)", fn, max_seqlen_q,
+                max_seqlen_k);
+    if (num_seqs == 0 || total_q == 0) return ok();
+    PKV_REQUIRE(q && k && v && o && cu_seqlens_q && cu_seqlens_k, PKV_ERR_INVALID_ARG,
+                "%s: a required pointer is NULL", fn);
+    PKV_REQUIRE(softmax_scale > 0.f, PKV_ERR_INVALID_ARG, "%s: softmax_scale must be > 0", fn);
+    const int64_t qw = (int64_t)num_q_heads * head_dim, kw = (int64_t)num_kv_heads * head_dim;
+    PKV_REQUIRE(q_row_stride >= qw, PKV_ERR_INVALID_ARG, "%s: q_row_stride %lld < num_q_heads*head_dim", fn,
+                (long long)q_row_stride);
+    PKV_REQUIRE(k_row_stride >= kw && v_row_stride >= kw, PKV_ERR_INVALID_ARG,
+                "%s: k/v row strides must be >= num_kv_heads*head_dim", fn);
+    PKV_REQUIRE(q_row_stride % 8 == 0 && k_row_stride % 8 == 0 && v_row_stride % 8 == 0, PKV_ERR_INVALID_ARG,
+                "%s: row strides must be multiples of 8 elements", fn);
+    PKV_REQUIRE(((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) % 16 == 0, PKV_ERR_INVALID_ARG,
+                "%s: tensors must be 16-byte aligned", fn);
+    if (block_table) {
+        PKV_REQUIRE(block_size == 256, PKV_ERR_UNSUPPORTED, "%s: block_size %d unsupported (only 256)", fn,
+                    block_size);
+        PKV_REQUIRE(max_blocks_per_seq > 0, PKV_ERR_INVALID_ARG, "%s: max_blocks_per_seq must be > 0", fn);
+        PKV_REQUIRE(num_blocks > 0, PKV_ERR_INVALID_ARG, "%s: num_blocks must be > 0", fn);
+        PKV_REQUIRE(k_row_stride == kw && v_row_stride == kw, PKV_ERR_INVALID_ARG,
+                    "%s: with a block table k/v are caches; row strides must equal num_kv_heads*head_dim", fn);
+        PKV_REQUIRE(k != v, PKV_ERR_INVALID_ARG, "%s: k_cache and v_cache must be distinct", fn);
+        PKV_REQUIRE((int64_t)max_seqlen_k <= (int64_t)max_blocks_per_seq * block_size, PKV_ERR_INVALID_ARG,
+                    "%s: max_seqlen_k %d exceeds the block table's capacity", fn, max_seqlen_k);
+    }
+    pkv::PrefillArgs a;
+    a.q = q;
+    a.q_row_stride = q_row_stride;
+    a.k = k;
+    a.k_row_stride = k_row_stride;
+    a.v = v;
+    a.v_row_stride = v_row_stride;
+    a.o = o;
+    a.cu_q = cu_seqlens_q;
+    a.cu_k = cu_seqlens_k;
+    a.num_seqs = num_seqs;
+    a.total_q = total_q;
+    a.max_seqlen_q = max_seqlen_q;
+    a.hq = num_q_heads;
+    a.hkv = num_kv_heads;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.block_table = block_table;
+    a.max_blocks = block_table ? max_blocks_per_seq : 0;
+    a.num_blocks = block_table ? num_blocks : 0;
+    return launched(pkv::launch_attn_prefill(a, (hipStream_t)stream), fn);
+}
+
+size_t pkv_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size) {
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads || head_dim != 128 ||
+        max_blocks_per_seq <= 0 || block_size != 256)
+        return 0;
+    if (num_seqs == 0) return 256;
+    return pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq);
+}
+
+int pkv_attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, void* o,
+                          const int32_t* context_lens, const int32_t* block_table, int32_t max_blocks_per_seq,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int64_t num_blocks, float softmax_scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    const char* fn = "pkv_attn_decode_paged";
+    int rc = check_heads(fn, num_q_heads, num_kv_heads, head_dim);
+    if (rc) return rc;
+    const int G = num_q_heads / num_kv_heads;
+    PKV_REQUIRE(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, PKV_ERR_UNSUPPORTED,
+                "%s: GQA group %d unsupported (1, 2, 4, 8 or 16)", fn, G);
+    PKV_REQUIRE(block_size == 256, PKV_ERR_UNSUPPORTED, "%s: block_size %d unsupported (only 256)", fn, block_size);
+    PKV_REQUIRE(num_seqs >= 0, PKV_ERR_INVALID_ARG, "%s: num_seqs must be >= 0", fn);
+    PKV_REQUIRE(max_blocks_per_seq > 0, PKV_ERR_INVALID_ARG, "%s: max_blocks_per_seq must be > 0", fn);
+    if (num_seqs == 0) return ok();
+    PKV_REQUIRE(q && k_cache && v_cache && o && context_lens && block_table, PKV_ERR_INVALID_ARG,
+                "%s: a required pointer is NULL", fn);
+    PKV_REQUIRE(k_cache != v_cache, PKV_ERR_INVALID_ARG, "%s: k_cache and v_cache must be distinct", fn);
+    PKV_REQUIRE(num_blocks > 0, PKV_ERR_INVALID_ARG, "%s: num_blocks must be > 0", fn);
+    PKV_REQUIRE(softmax_scale > 0.f, PKV_ERR_INVALID_ARG, "%s: softmax_scale must be > 0", fn);
+    PKV_REQUIRE(((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)o) % 16 == 0,
+                PKV_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
+    const size_t need = pkv_attn_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                        max_blocks_per_seq, block_size);
+    PKV_REQUIRE(workspace != nullptr && workspace_bytes >= need, PKV_ERR_WORKSPACE,
+                "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? workspace_bytes : (size_t)0);
+    PKV_REQUIRE((uintptr_t)workspace % 256 == 0, PKV_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+    pkv::DecodeArgs a;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.o = o;
+    a.context_lens = context_lens;
+    a.block_table = block_table;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.hq = num_q_heads;
+    a.hkv = num_kv_heads;
+    a.num_blocks = num_blocks;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.workspace = workspace;
+    return launched(pkv::launch_attn_decode(a, (hipStream_t)stream), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,294 @@
+// attn_prefill.hip -- varlen causal GQA prefill attention on MFMA (gfx950).
+//
+// What is computed: "3.3 Model skeleton and core operators", section 7.2, and
+// "nano-vllm code walkthrough", "Prefill stage": packed sequences delimited by
+// cu_seqlens, causal inside each sequence and nothing across sequences (the
+// block-diagonal mask of "同一个 Qwen3，两种写法" section 3.2, never built).
+// With a block table the keys come from the paged cache ("case 2", prefix hit
+// or a later chunk): query i of a sequence sits at absolute position
+// Lk - Lq + i.  q head h reads kv head h / (Hq/Hkv) ("Nano-vLLM 源码解读 #17
+// 注意力层", section 3).  The softmax is the exact online form of the same
+// page's section 5.2, in base 2 with the scale folded into the exponent.
+//
+// Design for CDNA4:
+//   * Transposed products keep every softmax statistic lane-local:
+//       S^T[key][q] = K . Q^T    and    O^T[d][q] += V^T . P^T
+//     on v_mfma_f32_32x32x16_bf16.  In the 32x32 accumulator layout a lane
+//     owns one column (one query row), so the running max, the rescale of O
+//     and the sum stay in registers; only the max needs one swap with the
+//     lane 32 away.  The S^T accumulator is, after exp2 and bf16 packing,
+//     already the B operand of the PV product.
+//   * A workgroup (4 waves, 32 query rows each) owns one kv head and the
+//     query heads of its GQA group that share it, so each K/V tile staged in
+//     LDS feeds 128 query rows.  K is kept row-major in LDS, V transposed
+//     (the PV contraction runs over keys), both padded against bank conflicts.
+//   * The next tile is loaded into registers while the current one is
+//     computed.  Tiles of 64 keys never straddle a 256-token block, so the
+//     paged loader does one block-table lookup per tile.
+//   * Causal tile skipping: a wave stops at the tile holding its last visible
+//     key; only tiles that cross the diagonal (or the sequence end) are masked.
+//   * Work order: longest query blocks first inside each (sequence, kv head),
+//     and consecutive work items share an XCD so their K/V stays in its L2.
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+
+namespace {
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kRowsPerWave = 32;
+constexpr int kKT = 64;                    // keys per tile
+constexpr int kKPitch = kHeadDim * 2 + 16;  // bytes per K row in LDS
+constexpr int kVPitch = kKT * 2 + 8;        // bytes per transposed V row in LDS
+}  // namespace
+
+template <int GW, bool PAGED>
+__global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int32_t m_blocks, int32_t n_work,
+                                                              int32_t head_groups) {
+    constexpr int kPosSub = kWaves / GW;                // position sub-blocks per workgroup
+    constexpr int kBM = kRowsPerWave * kPosSub;         // query positions per workgroup
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds[kKT * kKPitch];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds[kHeadDim * kVPitch];
+
+    const int work = xcd_remap(blockIdx.x, n_work);
+    if (work >= n_work) return;
+    // work = ((b * hkv + g) * head_groups + hg) * m_blocks + (m_blocks - 1 - mb)
+    const int mb = m_blocks - 1 - (work % m_blocks);
+    int rest = work / m_blocks;
+    const int hg = rest % head_groups;
+    rest /= head_groups;
+    const int g = rest % a.hkv;
+    const int b = rest / a.hkv;
+
+    const int cq0 = a.cu_q[b], cq1 = a.cu_q[b + 1];
+    const int ck0 = a.cu_k[b], ck1 = a.cu_k[b + 1];
+    const int Lq = cq1 - cq0, Lk = ck1 - ck0;
+    const int p0 = mb * kBM;
+    if (p0 >= Lq || Lk < Lq || Lq <= 0) return;
+    if (cq0 < 0 || cq1 > a.total_q || ck0 < 0) return;   // metadata outside the q/o rows: nothing is touched
+    const int off = Lk - Lq;                            // absolute position of query 0
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = a.hq / a.hkv;
+    const int head = g * G + hg * GW + (wave % GW);
+    const int wp0 = p0 + kRowsPerWave * (wave / GW);    // first query (sequence-relative) of this wave
+    const int wq_last = min(wp0 + kRowsPerWave, Lq) - 1;
+    const bool wave_live = wp0 < Lq;
+
+    // Keys any wave of this workgroup can see: 0 .. off + min(p0 + kBM, Lq) - 1.
+    const int wg_keys = off + min(p0 + kBM, Lq);
+    const int n_tiles = (wg_keys + kKT - 1) / kKT;
+    const int wave_keys = wave_live ? off + wq_last + 1 : 0;
+    const int wave_tiles = (wave_keys + kKT - 1) / kKT;
+
+    // ---- Q^T as the B operand: lane owns query row l%32, dims 8*(l/32) + 16*st .. +7.
+    const int qi = wp0 + (lane & 31);
+    const int q_row = cq0 + min(qi, Lq - 1);
+    bf16x8 qreg[8];
+    {
+        const uint16_t* qp = (const uint16_t*)a.q + (int64_t)min(q_row, a.total_q - 1) * a.q_row_stride +
+                             (int64_t)head * kHeadDim + 8 * (lane >> 5);
+#pragma unroll
+        for (int st = 0; st < 8; ++st) qreg[st] = __builtin_bit_cast(bf16x8, ldg128(qp + 16 * st));
+    }
+    const int qpos = off + qi;                          // absolute position of this lane's query
+
+    f32x16 oacc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+    float m_run = -INFINITY, l_part = 0.f;
+
+    // ---- tile loader: K as 4 x 16 B per thread (row-major), V as 4 keys x 8 dims per thread.
+    const int64_t krs = a.k_row_stride, vrs = a.v_row_stride;
+    const uint16_t* kbase = (const uint16_t*)a.k + (int64_t)g * kHeadDim;
+    const uint16_t* vbase = (const uint16_t*)a.v + (int64_t)g * kHeadDim;
+    const int32_t* bt = PAGED ? a.block_table + (int64_t)b * a.max_blocks : nullptr;
+    auto tile_row0 = [&](int j0, bool& ok) -> int64_t {
+        // cache / array row of key j0 (tiles never straddle a 256-token block)
+        if (PAGED) {
+            const int bi = j0 / kBlockSize;
+            const int32_t blk = bi < a.max_blocks ? bt[bi] : -1;
+            ok = blk >= 0 && (int64_t)blk < a.num_blocks;
+            return ok ? (int64_t)blk * kBlockSize + (j0 % kBlockSize) : 0;
+        } else {
+            ok = true;
+            return (int64_t)ck0 + j0;
+        }
+    };
+    u32x4 kst[4], vst[4];
+    auto load_tile = [&](int t) {
+        const int j0 = t * kKT;
+        bool ok;
+        const int64_t r0 = tile_row0(j0, ok);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + kThreads * i;             // 16-byte chunk of the 64 x 256 B K tile
+            const int key = c >> 4, piece = c & 15;
+            const bool in = ok && (j0 + key) < Lk;
+            kst[i] = in ? ldg128(kbase + (r0 + key) * krs + piece * 8) : u32x4{0u, 0u, 0u, 0u};
+        }
+        const int kq = tid >> 4, dg = tid & 15;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int key = 4 * kq + r;
+            const bool in = ok && (j0 + key) < Lk;
+            vst[r] = in ? ldg128(vbase + (r0 + key) * vrs + dg * 8) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + kThreads * i;
+            const int key = c >> 4, piece = c & 15;
+            *reinterpret_cast<u32x4*>(k_lds + key * kKPitch + piece * 16) = kst[i];
+        }
+        // transpose 4 keys x 8 dims -> 8 rows (dims) of 4 keys
+        const int kq = tid >> 4, dg = tid & 15;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            // dims 8dg + 2e2 (low halves) and 8dg + 2e2 + 1 (high halves)
+            const uint32_t a0 = vst[0][e2], a1 = vst[1][e2], a2 = vst[2][e2], a3 = vst[3][e2];
+            u32x2 lo, hi;
+            lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);   // keys 0,1 of the even dim
+            lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);   // keys 2,3
+            hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // keys 0,1 of the odd dim
+            hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
+            const int d0 = 8 * dg + 2 * e2;
+            *reinterpret_cast<u32x2*>(v_lds + d0 * kVPitch + kq * 8) = lo;
+            *reinterpret_cast<u32x2*>(v_lds + (d0 + 1) * kVPitch + kq * 8) = hi;
+        }
+    };
+
+    const int h32 = lane >> 5;  // which half of the k-slots this lane feeds
+    load_tile(0);
+    for (int t = 0; t < n_tiles; ++t) {
+        __syncthreads();          // all waves are done with the previous tile
+        store_tile();
+        __syncthreads();
+        if (t + 1 < n_tiles) load_tile(t + 1);
+        if (t >= wave_tiles) continue;   // past this wave's last visible key
+
+        const int j0 = t * kKT;
+        bool ok;
+        (void)tile_row0(j0, ok);
+        // ---- S^T = K Q^T for two 32-key halves
+        f32x16 s[2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kh][r] = 0.f;
+            const unsigned char* kr = k_lds + (32 * kh + (lane & 31)) * kKPitch + 16 * h32;
+#pragma unroll
+            for (int st = 0; st < 8; ++st) {
+                const bf16x8 av = *reinterpret_cast<const bf16x8*>(kr + 32 * st);
+                s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[st], s[kh], 0, 0, 0);
+            }
+        }
+        // s[kh][r] = score of key j0 + 32kh + 8(r/4) + 4*h32 + r%4 for query qi.
+        const bool need_mask = !ok || (j0 + kKT - 1 > off + wp0) || (j0 + kKT > Lk);
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float v = s[kh][r] * a.scale_log2;
+                if (need_mask) {
+                    const int kp = j0 + 32 * kh + 8 * (r >> 2) + 4 * h32 + (r & 3);
+                    v = (!ok || kp > qpos || kp >= Lk) ? -INFINITY : v;
+                }
+                s[kh][r] = v;
+                tmax = fmaxf(tmax, v);
+            }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float mn = fmaxf(m_run, tmax);
+        const float ref = mn == -INFINITY ? 0.f : mn;
+        const float alpha = exp2f(m_run - ref);
+        m_run = mn;
+        float psum = 0.f;
+        uint32_t pk[2][8];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float e0 = exp2f(s[kh][r] - ref), e1 = exp2f(s[kh][r + 1] - ref);
+                psum += e0 + e1;
+                pk[kh][r >> 1] = pack_bf16x2(e0, e1);
+            }
+        l_part = l_part * alpha + psum;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+
+        // ---- O^T += V^T P^T: per 16-key step (kh, v) the B operand is registers 8v..8v+7 of s[kh].
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                u32x4 bw = {pk[kh][4 * v], pk[kh][4 * v + 1], pk[kh][4 * v + 2], pk[kh][4 * v + 3]};
+                const bf16x8 bv = __builtin_bit_cast(bf16x8, bw);
+                const int kcol = 32 * kh + 16 * v + 4 * h32;   // first key of this lane's k-slots
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    const unsigned char* vr = v_lds + (32 * dt + (lane & 31)) * kVPitch + 2 * kcol;
+                    const u32x2 x0 = *reinterpret_cast<const u32x2*>(vr);
+                    const u32x2 x1 = *reinterpret_cast<const u32x2*>(vr + 16);
+                    u32x4 aw = {x0[0], x0[1], x1[0], x1[1]};
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, aw), bv, oacc[dt],
+                                                                       0, 0, 0);
+                }
+            }
+    }
+
+    // ---- normalise and store: lane holds O^T[d][qi] for d = 32dt + 8(r/4) + 4*h32 + r%4.
+    if (!wave_live || qi >= Lq) return;
+    const float l = l_part + __shfl_xor(l_part, 32, 64);
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const int orow = cq0 + qi;
+    if (orow >= a.total_q) return;
+    uint16_t* op = (uint16_t*)a.o + ((int64_t)orow * a.hq + head) * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int d = 32 * dt + 8 * r4 + 4 * h32;
+            u32x2 w;
+            w[0] = pack_bf16x2(oacc[dt][4 * r4] * inv, oacc[dt][4 * r4 + 1] * inv);
+            w[1] = pack_bf16x2(oacc[dt][4 * r4 + 2] * inv, oacc[dt][4 * r4 + 3] * inv);
+            *reinterpret_cast<u32x2*>(op + d) = w;
+        }
+}
+
+hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t stream) {
+    if (a.num_seqs == 0 || a.total_q == 0 || a.max_seqlen_q == 0) return hipSuccess;
+    const int G = a.hq / a.hkv;
+    const int gw = G >= 4 ? 4 : G;                 // query heads per workgroup
+    if (G % gw) return hipErrorInvalidValue;
+    const int head_groups = G / gw;
+    const int bm = kRowsPerWave * (kWaves / gw);
+    const int m_blocks = (a.max_seqlen_q + bm - 1) / bm;
+    const int64_t n_work64 = (int64_t)a.num_seqs * a.hkv * head_groups * m_blocks;
+    if (n_work64 > (int64_t)0x7FFFFFF0) return hipErrorInvalidValue;
+    const int n_work = (int)n_work64;
+    const int grid = ((n_work + 7) / 8) * 8;
+    const bool paged = a.block_table != nullptr;
+#define PKV_PREFILL(GW_, PG_)                                                                                  \
+    hipLaunchKernelGGL((prefill_kernel<GW_, PG_>), dim3(grid), dim3(kThreads), 0, stream, a, m_blocks, n_work, \
+                       head_groups)
+    if (gw == 4) {
+        if (paged) PKV_PREFILL(4, true); else PKV_PREFILL(4, false);
+    } else if (gw == 2) {
+        if (paged) PKV_PREFILL(2, true); else PKV_PREFILL(2, false);
+    } else if (gw == 1) {
+        if (paged) PKV_PREFILL(1, true); else PKV_PREFILL(1, false);
+    } else {
+        return hipErrorInvalidValue;
+    }
+#undef PKV_PREFILL
+    return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,62 @@
+// pkv_device.h -- device-side types and helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHeadDim = 128;
+constexpr int kBlockSize = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// bf16 bit pattern held in the low / high half of a 32-bit word -> fp32 (exact).
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 v = {(bf16)lo, (bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ u32x4 ldg128(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void stg128(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Non-temporal 128-bit global load: streamed data that is read exactly once.
+__device__ __forceinline__ u32x4 ldg128_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Launch-order remap so that consecutive work items land on the same XCD.
+// Workgroups are dispatched round-robin over the 8 XCDs: id -> XCD id % 8.
+// Item k of XCD x's share gets work index x * per + k.  Ids past the share
+// sizes map to >= n and are skipped by the caller.
+__device__ __forceinline__ int xcd_remap(int id, int n) {
+    const int per = (n + 7) >> 3;
+    const int x = id & 7;
+    const int k = id >> 3;
+    return x * per + k;
+}
+
+}  // namespace pkv

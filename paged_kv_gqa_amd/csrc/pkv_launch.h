@@ -1,0 +1,68 @@
+// pkv_launch.h -- host-side launchers (internal C++ interface between the
+// validating C entry points and the kernel translation units).  Arguments
+// reaching these functions have been validated by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+hipError_t launch_rope_cache_build(float* table, int32_t max_pos, int32_t rot_dim, double theta,
+                                   hipStream_t stream);
+
+hipError_t launch_qk_norm_rope(const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride,
+                               void* q_out, void* k_out, const int64_t* positions, int32_t n_tokens,
+                               int32_t hq, int32_t hkv, const void* gq, const void* gk, float eps,
+                               const float* table, int32_t max_pos, hipStream_t stream);
+
+hipError_t launch_store_kvcache(const void* key, int64_t key_row_stride, const void* value,
+                                int64_t value_row_stride, void* k_cache, void* v_cache, int64_t num_slots,
+                                const int32_t* slot_mapping, int32_t n_tokens, int64_t row_bytes,
+                                int32_t elem_bytes, hipStream_t stream);
+
+struct PrefillArgs {
+    const void* q;
+    int64_t q_row_stride;
+    const void* k;
+    int64_t k_row_stride;
+    const void* v;
+    int64_t v_row_stride;
+    void* o;
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    int32_t num_seqs;
+    int32_t total_q;
+    int32_t max_seqlen_q;
+    int32_t hq;
+    int32_t hkv;
+    float scale_log2;            // softmax_scale * log2(e)
+    const int32_t* block_table;  // NULL: contiguous K/V
+    int32_t max_blocks;
+    int64_t num_blocks;
+};
+hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    void* o;
+    const int32_t* context_lens;
+    const int32_t* block_table;
+    int32_t max_blocks;
+    int32_t num_seqs;
+    int32_t hq;
+    int32_t hkv;
+    int64_t num_blocks;
+    float scale_log2;
+    void* workspace;
+};
+// Number of 256-token blocks one split-K work item covers, and the number of
+// splits per sequence the workspace is sized for.
+int decode_split_blocks(int32_t num_seqs, int32_t hkv, int32_t max_blocks);
+size_t decode_workspace_bytes(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t max_blocks);
+hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace pkv

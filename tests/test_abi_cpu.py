@@ -1,0 +1,119 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects invalid arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_gqa_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    with open(os.path.join(ROOT, "include", "pkv.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"PKV_API\s+[\w\s\*]+?\b(pkv_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pkv.LIB_PATH):
+        pytest.skip("libpkv.so not built (run python -m paged_kv_gqa_amd.build)")
+    return pkv.load_library()
+
+
+def test_header_declares_the_four_steps():
+    syms = _declared_symbols()
+    for s in ("pkv_qk_norm_rope", "pkv_store_kvcache", "pkv_attn_prefill_varlen", "pkv_attn_decode_paged"):
+        assert s in syms
+    assert sorted(pkv.EXPORTED) == syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for s in _declared_symbols():
+        assert hasattr(lib, s), s
+    assert lib.pkv_version() >> 16 == 1
+
+
+FAKE = ctypes.c_void_p(0x1000)     # never dereferenced: validation fails first
+
+
+def _err(lib):
+    return lib.pkv_last_error().decode()
+
+
+def test_qk_norm_rope_validation(lib):
+    f = lib.pkv_qk_norm_rope
+    # Hq not a multiple of Hkv
+    assert f(FAKE, 2048, FAKE, 1024, FAKE, FAKE, FAKE, 4, 12, 8, 128, FAKE, FAKE, 1e-6, FAKE, 40960, None) == -1
+    assert "multiple" in _err(lib)
+    # head_dim other than 128
+    assert f(FAKE, 2048, FAKE, 1024, FAKE, FAKE, FAKE, 4, 16, 8, 64, FAKE, FAKE, 1e-6, FAKE, 40960, None) == -2
+    # row stride shorter than the row
+    assert f(FAKE, 1024, FAKE, 1024, FAKE, FAKE, FAKE, 4, 16, 8, 128, FAKE, FAKE, 1e-6, FAKE, 40960, None) == -1
+    # null pointer
+    assert f(None, 2048, FAKE, 1024, FAKE, FAKE, FAKE, 4, 16, 8, 128, FAKE, FAKE, 1e-6, FAKE, 40960, None) == -1
+    # negative token count; zero tokens is a no-op success
+    assert f(FAKE, 2048, FAKE, 1024, FAKE, FAKE, FAKE, -1, 16, 8, 128, FAKE, FAKE, 1e-6, FAKE, 40960, None) == -1
+    assert f(None, 2048, None, 1024, None, None, None, 0, 16, 8, 128, None, None, 1e-6, None, 40960, None) == 0
+    # in place with a strided input is refused
+    assert f(FAKE, 4096, FAKE, 4096, FAKE, ctypes.c_void_p(0x2000), FAKE, 4, 16, 8, 128, FAKE, FAKE, 1e-6, FAKE,
+             40960, None) == -1
+
+
+def test_store_kvcache_validation(lib):
+    f = lib.pkv_store_kvcache
+    ok_args = [FAKE, 1024, FAKE, 1024, FAKE, ctypes.c_void_p(0x2000), 2048, FAKE, 4, 8, 128, 2, None]
+    bad = list(ok_args); bad[1] = 512        # key stride < D
+    assert f(*bad) == -1 and "stride" in _err(lib)
+    bad = list(ok_args); bad[11] = 3         # element size
+    assert f(*bad) == -1
+    bad = list(ok_args); bad[7] = None       # slot_mapping missing
+    assert f(*bad) == -1
+    bad = list(ok_args); bad[5] = FAKE       # k_cache == v_cache
+    assert f(*bad) == -1
+    bad = list(ok_args); bad[8] = 0          # zero tokens: nothing to do
+    assert f(*bad) == 0
+
+
+def test_prefill_validation(lib):
+    f = lib.pkv_attn_prefill_varlen
+    base = [FAKE, 4096, FAKE, 4096, FAKE, 4096, FAKE, FAKE, FAKE, 2, 337, 300, 300, 16, 8, 128, 0.088, 1, None, 0,
+            256, 0, None]
+    a = list(base); a[17] = 0                # causal = 0 is not built
+    assert f(*a) == -2
+    a = list(base); a[13] = 12               # Hq % Hkv
+    assert f(*a) == -1
+    a = list(base); a[11] = 400              # max_seqlen_q > max_seqlen_k
+    assert f(*a) == -1
+    a = list(base); a[18] = FAKE; a[19] = 2; a[21] = 8   # paged with strided k/v rows
+    assert f(*a) == -1 and "caches" in _err(lib)
+    a = list(base); a[18] = FAKE; a[3] = a[5] = 1024; a[19] = 2; a[20] = 128; a[21] = 8   # block size 128
+    assert f(*a) == -2
+    a = list(base); a[9] = 0                 # no sequences: no-op
+    assert f(*a) == 0
+
+
+def test_decode_validation_and_workspace(lib):
+    ws = lib.pkv_attn_decode_workspace_bytes
+    assert ws(64, 16, 8, 128, 32, 256) > 0
+    assert ws(64, 16, 8, 64, 32, 256) == 0          # head_dim
+    assert ws(64, 12, 8, 128, 32, 256) == 0         # Hq % Hkv
+    f = lib.pkv_attn_decode_paged
+    need = ws(4, 32, 8, 128, 16, 256)
+    base = [FAKE, FAKE, ctypes.c_void_p(0x2000), FAKE, FAKE, FAKE, 16, 4, 32, 8, 128, 256, 100, 0.088,
+            ctypes.c_void_p(0x10000), need, None]
+    a = list(base); a[15] = need - 1                 # workspace too small
+    assert f(*a) == -4
+    a = list(base); a[14] = ctypes.c_void_p(0x10010)  # misaligned workspace
+    assert f(*a) == -4
+    a = list(base); a[11] = 16                        # block size
+    assert f(*a) == -2
+    a = list(base); a[8] = 24                         # group of 3
+    assert f(*a) == -2
+    a = list(base); a[12] = 0                         # empty pool
+    assert f(*a) == -1
+    a = list(base); a[7] = 0                          # empty batch
+    assert f(*a) == 0

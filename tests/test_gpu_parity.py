@@ -1,0 +1,472 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every input comes from the seeded generators in ``workloads``; every expected
+value from ``oracle``.  Gates are in tests/gpu_helpers.py.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_gqa_amd as pkv
+import workloads as wl
+from gpu_helpers import (bits, check_attn, check_ulp, f64, gather_sequences, to_dev)
+
+pytestmark = pytest.mark.gpu
+D = 128
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pkv.load_library()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def table_dev(dev):
+    return pkv.rope_cache_build(40960, D, 1e6, device=dev)
+
+
+@pytest.fixture(scope="module")
+def table_host():
+    return oracle.rope_table(40960, D, 1e6)
+
+
+def _say(*a):
+    print("[gpu]", *a, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# RoPE table and QK-Norm + RoPE
+# ---------------------------------------------------------------------------
+
+def test_rope_table_matches_oracle(dev, table_dev, table_host):
+    _say("rope table 40960 x 128")
+    got = table_dev.cpu().numpy()
+    ulps = np.abs(got.view(np.int32).astype(np.int64) - table_host.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1, f"table differs by {ulps.max()} fp32 ulps"
+
+
+def _norm_rope_case(dev, table_dev, table_host, shape, qkv, gq, gk, pos):
+    q0, k0, _ = wl.qkv_views(shape)
+    n = qkv.shape[0]
+    qkv_d = to_dev(qkv, dev)
+    q = qkv_d[:, q0:k0].view(n, shape.num_q_heads, D)
+    k = qkv_d[:, k0:k0 + shape.kv_size].view(n, shape.num_kv_heads, D)
+    pos_d = to_dev(pos.astype(np.int64), dev)
+    qo, ko = pkv.qk_norm_rope(q, k, pos_d, to_dev(gq, dev), to_dev(gk, dev), table_dev, shape.eps)
+    torch.cuda.synchronize()
+    ref_q = oracle.rmsnorm_rope(qkv, shape.num_q_heads, D, gq, shape.eps, pos, table_host, col_offset=q0)
+    ref_k = oracle.rmsnorm_rope(qkv, shape.num_kv_heads, D, gk, shape.eps, pos, table_host, col_offset=k0)
+    check_ulp(bits(qo).reshape(ref_q.shape), ref_q, oracle.round_bf16(ref_q), "q'")
+    check_ulp(bits(ko).reshape(ref_k.shape), ref_k, oracle.round_bf16(ref_k), "k'")
+    return qkv_d, qo, ko
+
+
+def test_qk_norm_rope_tiny(dev, table_dev, table_host):
+    _say("qk_norm_rope on the two-sequence chain (337 tokens, 16/8 heads)")
+    w = wl.tiny_chain(seed=0)
+    qkv_d, qo, ko = _norm_rope_case(dev, table_dev, table_host, w.shape, w.qkv, w.gamma_q, w.gamma_k, w.positions)
+    # in place on contiguous copies gives the same bits
+    n = w.qkv.shape[0]
+    qc = qkv_d[:, :2048].contiguous().view(n, 16, D)
+    kc = qkv_d[:, 2048:3072].contiguous().view(n, 8, D)
+    pkv.qk_norm_rope(qc, kc, to_dev(w.positions, dev), to_dev(w.gamma_q, dev), to_dev(w.gamma_k, dev), table_dev,
+                     1e-6, q_out=qc, k_out=kc)
+    torch.cuda.synchronize()
+    assert torch.equal(qc, qo) and torch.equal(kc, ko)
+
+
+def test_qk_norm_rope_8b_long_positions(dev, table_dev, table_host):
+    _say("qk_norm_rope 8B shapes, 777 tokens, positions up to 40959")
+    s = wl.QWEN3_8B
+    rng = wl.rng_for(90, 0, 0)
+    qkv = wl.normal_bf16(rng, (777, s.qkv_width), scale=3.0)
+    gq, gk = wl.gamma_bf16(rng), wl.gamma_bf16(rng)
+    pos = rng.integers(0, 40960, size=777).astype(np.int64)
+    pos[:2] = [0, 40959]
+    _norm_rope_case(dev, table_dev, table_host, s, qkv, gq, gk, pos)
+
+
+# ---------------------------------------------------------------------------
+# store_kvcache
+# ---------------------------------------------------------------------------
+
+def _store_raw(key, value, kc, vc, slots, hkv, hd, key_stride=None, value_stride=None):
+    lib = pkv.load_library()
+    rc = lib.pkv_store_kvcache(key.data_ptr(), key_stride or hkv * hd, value.data_ptr(), value_stride or hkv * hd,
+                               kc.data_ptr(), vc.data_ptr(), kc.numel() // (hkv * hd), slots.data_ptr(),
+                               slots.numel(), hkv, hd, key.element_size(),
+                               torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, lib.pkv_last_error()
+
+
+def test_store_kvcache_printed_examples(dev, golden):
+    _say("store_kvcache printed examples (fp32 rows)")
+    g = golden("scatter_skeleton_w3.json")
+    src = torch.tensor(g["src"], dtype=torch.float32, device=dev)
+    dk, dv = torch.zeros(3, 4, device=dev), torch.zeros(3, 4, device=dev)
+    _store_raw(src, src, dk, dv, torch.tensor(g["slot"], dtype=torch.int32, device=dev), 1, 4)
+    torch.cuda.synchronize()
+    assert dk.cpu().tolist() == g["expected_dst"]
+    g = golden("store_kvcache_w4.json")
+    base = torch.arange(4).reshape(1, 2, 2)
+    key = (torch.arange(4).reshape(4, 1, 1) * 10 + base).float().to(dev)
+    value = key + 100
+    kc = torch.zeros(g["cache_shape"], device=dev)
+    vc = torch.zeros(g["cache_shape"], device=dev)
+    _store_raw(key, value, kc, vc, torch.tensor(g["slot_mapping"], dtype=torch.int32, device=dev), 2, 2)
+    torch.cuda.synchronize()
+    assert kc.view(-1, 4).cpu().tolist() == g["expected_k_cache_rows"]
+    assert vc.view(-1, 4)[0].cpu().tolist() == g["expected_v_cache_slot0"]
+
+
+def _store_vs_oracle(dev, key_np, val_np, slots, num_blocks, hkv, key_stride, val_stride, seed):
+    """Random bytes in the caches first: every byte the scatter must not touch is checked too."""
+    rng = np.random.default_rng(seed)
+    kc0 = rng.integers(0, 65536, size=(num_blocks, 256, hkv, D), dtype=np.uint16)
+    vc0 = rng.integers(0, 65536, size=(num_blocks, 256, hkv, D), dtype=np.uint16)
+    kc, vc = to_dev(kc0, dev), to_dev(vc0, dev)
+    kd, vd = to_dev(key_np, dev), to_dev(val_np, dev)
+    n = slots.shape[0]
+    key_v = torch.as_strided(kd, (n, hkv, D), (key_stride, D, 1))
+    val_v = torch.as_strided(vd, (n, hkv, D), (val_stride, D, 1), storage_offset=0)
+    pkv.store_kvcache(key_v, val_v, kc, vc, to_dev(slots, dev))
+    torch.cuda.synchronize()
+    ek, ev = kc0.copy(), vc0.copy()
+    oracle.store_kvcache(key_np, val_np, ek, ev, slots, key_row_stride=key_stride, value_row_stride=val_stride,
+                         row_elems=hkv * D)
+    assert np.array_equal(bits(kc).reshape(ek.shape), ek)
+    assert np.array_equal(bits(vc).reshape(ev.shape), ev)
+
+
+def test_store_kvcache_bit_exact_tiny_chain(dev):
+    _say("store_kvcache tiny chain, v as a strided view of qkv")
+    w = wl.tiny_chain(seed=0)
+    n = w.qkv.shape[0]
+    key = np.ascontiguousarray(w.qkv[:, 2048:3072])          # contiguous k rows
+    val = np.ascontiguousarray(w.qkv[:, 3072:])              # v columns of qkv: row stride 4096 below
+    qkv_v = np.zeros((n, 4096), np.uint16)
+    qkv_v[:, :1024] = val
+    slots = w.slot_mapping.copy()
+    slots[5] = -1                                             # one padding token
+    _store_vs_oracle(dev, key, qkv_v, slots, w.num_blocks, 8, 1024, 4096, seed=1)
+
+
+def test_store_kvcache_bit_exact_8b_prefill(dev):
+    _say("store_kvcache 32768 tokens (8B prefix workload)")
+    w = wl.prefix_prefill_8b(seed=0)
+    rng = wl.rng_for(91, 0, 0)
+    key = rng.integers(0, 65536, size=(w.num_q_tokens, 1024), dtype=np.uint16)
+    val = rng.integers(0, 65536, size=(w.num_q_tokens, 1024), dtype=np.uint16)
+    _store_vs_oracle(dev, key, val, w.slot_mapping, w.num_blocks, 8, 1024, 1024, seed=2)
+
+
+def test_store_kvcache_skips_out_of_range_slots(dev):
+    _say("store_kvcache with -1 and out-of-range slots")
+    rng = np.random.default_rng(3)
+    key = rng.integers(0, 65536, size=(6, 1024), dtype=np.uint16)
+    slots = np.array([0, -1, 511, 512, -7, 3], np.int32)     # pool of 2 blocks = 512 slots
+    _store_vs_oracle(dev, key, key.copy(), slots, 2, 8, 1024, 1024, seed=4)
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+
+def _prefill_case(dev, lens_q, lens_k, hq, hkv, seed, paged=False, num_blocks=None, rows=None):
+    rng = wl.rng_for(92, seed, 0)
+    cuq, cuk = wl.cu_seqlens(lens_q), wl.cu_seqlens(lens_k)
+    tq, tk = int(cuq[-1]), int(cuk[-1])
+    q = wl.normal_bf16(rng, (tq, hq, D))
+    k = wl.normal_bf16(rng, (tk, hkv, D))
+    v = wl.normal_bf16(rng, (tk, hkv, D))
+    if not paged:
+        o = pkv.attn_prefill_varlen(to_dev(q, dev), to_dev(k, dev), to_dev(v, dev), to_dev(cuq, dev),
+                                    to_dev(cuk, dev), max(lens_q), max(lens_k))
+        torch.cuda.synchronize()
+        ref = oracle.attn_prefill(q, k, v, cuq, cuk, hq, hkv, rows=rows)
+        return o, ref, (q, k, v, cuq, cuk)
+    nb = num_blocks or sum(-(-L // 256) for L in lens_k) + 3
+    perm = rng.permutation(nb)
+    kc = wl.normal_bf16(rng, (nb * 256, hkv, D))
+    vc = wl.normal_bf16(rng, (nb * 256, hkv, D))
+    rows_bt, nxt, off = [], 0, 0
+    for L in lens_k:
+        c = -(-L // 256)
+        rows_bt.append(list(perm[nxt:nxt + c]))
+        nxt += c
+    bt = wl.pad_block_tables(rows_bt)
+    for b, L in enumerate(lens_k):
+        sl = wl.slots_for(bt[b], np.arange(L))
+        kc[sl] = k[off:off + L]
+        vc[sl] = v[off:off + L]
+        off += L
+    o = pkv.attn_prefill_varlen(to_dev(q, dev), to_dev(kc.reshape(nb, 256, hkv, D), dev),
+                                to_dev(vc.reshape(nb, 256, hkv, D), dev), to_dev(cuq, dev), to_dev(cuk, dev),
+                                max(lens_q), max(lens_k), block_table=to_dev(bt, dev))
+    torch.cuda.synchronize()
+    ref = oracle.attn_prefill(q, kc, vc, cuq, cuk, hq, hkv, block_table=bt, rows=rows)
+    return o, ref, (q, kc, vc, cuq, cuk, bt)
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 8), (8, 8)])
+def test_prefill_varlen_ragged(dev, hq, hkv):
+    lens = [1, 37, 63, 64, 65, 129, 300]
+    _say(f"prefill case 1, lengths {lens}, {hq}/{hkv} heads")
+    o, ref, _ = _prefill_case(dev, lens, lens, hq, hkv, seed=hq + hkv)
+    check_attn(f64(o), ref, "prefill ragged")
+
+
+def test_prefill_paged_prefix(dev):
+    lk, lq = [300, 513, 64, 1000], [40, 257, 64, 1]
+    _say(f"prefill case 2 (paged), Lk {lk}, Lq {lq}")
+    o, ref, _ = _prefill_case(dev, lq, lk, 32, 8, seed=5, paged=True)
+    check_attn(f64(o), ref, "prefill paged")
+
+
+def test_prefill_paged_equals_contiguous(dev):
+    lens = [100, 257, 512, 700]
+    _say("prefill: paged and contiguous loaders give the same bits")
+    o1, _, inp = _prefill_case(dev, lens, lens, 16, 8, seed=6)
+    q, k, v, cuq, cuk = inp
+    nb = sum(-(-L // 256) for L in lens) + 2
+    perm = np.random.default_rng(7).permutation(nb)
+    kc = np.zeros((nb * 256, 8, D), np.uint16)
+    vc = np.zeros_like(kc)
+    rows_bt, nxt, off = [], 0, 0
+    for L in lens:
+        c = -(-L // 256)
+        rows_bt.append(list(perm[nxt:nxt + c]))
+        nxt += c
+    bt = wl.pad_block_tables(rows_bt)
+    for b, L in enumerate(lens):
+        sl = wl.slots_for(bt[b], np.arange(L))
+        kc[sl], vc[sl] = k[off:off + L], v[off:off + L]
+        off += L
+    o2 = pkv.attn_prefill_varlen(to_dev(q, dev), to_dev(kc.reshape(nb, 256, 8, D), dev),
+                                 to_dev(vc.reshape(nb, 256, 8, D), dev), to_dev(cuq, dev), to_dev(cuk, dev),
+                                 max(lens), max(lens), block_table=to_dev(bt, dev))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_prefill_varlen_workload_sampled(dev):
+    w = wl.varlen_prefill(seed=0)
+    s = w.shape
+    _say(f"prefill 0.6B varlen workload, lengths {list(w.lengths)}")
+    qkv = w.qkv()
+    n = qkv.shape[0]
+    q0, k0, v0 = wl.qkv_views(s)
+    qkv_d = to_dev(qkv, dev)
+    q = qkv_d[:, q0:k0].view(n, 16, D)
+    k = qkv_d[:, k0:v0].view(n, 8, D)
+    v = qkv_d[:, v0:].view(n, 8, D)
+    cu = to_dev(w.cu_seqlens, dev)
+    L = int(w.lengths.max())
+    o = pkv.attn_prefill_varlen(q, k, v, cu, cu, L, L)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    t = np.concatenate([rng.integers(0, n, 1500), w.cu_seqlens[:-1], w.cu_seqlens[1:] - 1])
+    h = rng.integers(0, 16, t.shape[0])
+    rows = np.stack([t, h], 1)
+    ref = oracle.attn_prefill(qkv, qkv, qkv, w.cu_seqlens, w.cu_seqlens, 16, 8, rows=rows, q_row_stride=4096,
+                              k_row_stride=4096, v_row_stride=4096, q_col=q0, k_col=k0, v_col=v0)
+    got = f64(o)[t, h]
+    check_attn(got, ref, "prefill 0.6B varlen")
+
+
+def test_prefill_prefix_workload_sampled(dev):
+    w = wl.prefix_prefill_8b(seed=0)
+    _say("prefill 8B prefix-hit workload (16 x 2048 queries over 4096 keys), sampled rows")
+    rng = wl.rng_for(93, 0, 0)
+    hkv, hq = 8, 32
+    kc = torch.empty((w.num_blocks, 256, hkv, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    wl.fill_normal_bf16_(kc, 5, 0, 10)
+    wl.fill_normal_bf16_(vc, 5, 0, 11)
+    q = to_dev(wl.normal_bf16(rng, (w.num_q_tokens, hq, D)), dev)
+    o = pkv.attn_prefill_varlen(q, kc, vc, to_dev(w.cu_seqlens_q, dev), to_dev(w.cu_seqlens_k, dev), 2048, 4096,
+                                block_table=to_dev(w.block_tables, dev))
+    torch.cuda.synchronize()
+    r = np.random.default_rng(9)
+    t = np.concatenate([r.integers(0, w.num_q_tokens, 300), [0, 2047, 2048, w.num_q_tokens - 1]])
+    h = r.integers(0, hq, t.shape[0])
+    ref = oracle.attn_prefill(bits(q), bits(kc).reshape(-1, hkv, D), bits(vc).reshape(-1, hkv, D), w.cu_seqlens_q,
+                              w.cu_seqlens_k, hq, hkv, block_table=w.block_tables, rows=np.stack([t, h], 1))
+    check_attn(f64(o)[t, h], ref, "prefill 8B prefix")
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+def _decode_case(dev, ctx, hq, hkv, seed, nan_canaries=False, permute=False):
+    rng = wl.rng_for(94, seed, 0)
+    B = len(ctx)
+    mb = max(-(-c // 256) for c in ctx) + 1
+    nb = sum(-(-c // 256) for c in ctx) + 3
+    perm = rng.permutation(nb)
+    rows_bt, nxt = [], 0
+    for c in ctx:
+        n = -(-c // 256)
+        rows_bt.append(list(perm[nxt:nxt + n]))
+        nxt += n
+    bt = wl.pad_block_tables(rows_bt, mb)
+    kc = wl.normal_bf16(rng, (nb, 256, hkv, D))
+    vc = wl.normal_bf16(rng, (nb, 256, hkv, D))
+    q = wl.normal_bf16(rng, (B, hq, D))
+    cl = np.array(ctx, np.int32)
+    o = pkv.attn_decode_paged(to_dev(q, dev), to_dev(kc, dev), to_dev(vc, dev), to_dev(cl, dev), to_dev(bt, dev))
+    torch.cuda.synchronize()
+    ref = oracle.attn_decode(q, kc.reshape(-1, hkv, D), vc.reshape(-1, hkv, D), cl, bt, hq, hkv)
+    out = {"o": o, "ref": ref}
+    if nan_canaries:
+        kc2, vc2 = kc.copy(), vc.copy()
+        used = np.zeros((nb, 256), bool)
+        for b, c in enumerate(ctx):
+            for j in range(c):
+                used[bt[b, j // 256], j % 256] = True
+        kc2[~used] = 0x7FC0
+        vc2[~used] = 0x7FC0
+        out["o_nan"] = pkv.attn_decode_paged(to_dev(q, dev), to_dev(kc2, dev), to_dev(vc2, dev), to_dev(cl, dev),
+                                             to_dev(bt, dev))
+    if permute:
+        p = rng.permutation(nb)
+        kc3 = np.empty_like(kc)
+        vc3 = np.empty_like(vc)
+        kc3[p] = kc
+        vc3[p] = vc
+        bt3 = np.where(bt >= 0, p[np.maximum(bt, 0)], -1).astype(np.int32)
+        out["o_perm"] = pkv.attn_decode_paged(to_dev(q, dev), to_dev(kc3, dev), to_dev(vc3, dev), to_dev(cl, dev),
+                                              to_dev(bt3, dev))
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 8), (8, 8)])
+def test_decode_small_ragged(dev, hq, hkv):
+    ctx = [1, 2, 255, 256, 257, 300, 1000, 4097, 0]
+    _say(f"decode contexts {ctx}, {hq}/{hkv} heads, NaN canaries, permuted pool")
+    r = _decode_case(dev, ctx, hq, hkv, seed=hq, nan_canaries=True, permute=True)
+    got = f64(r["o"])
+    check_attn(got[:-1], r["ref"][:-1], "decode small")
+    assert np.all(got[-1] == 0.0), "zero-length context must give a zero row"
+    assert torch.equal(r["o"], r["o_nan"]), "bytes outside the context changed the output"
+    assert torch.equal(r["o"], r["o_perm"]), "physical block placement changed the output"
+
+
+def test_decode_long_context_many_splits(dev):
+    ctx = [32768, 20000, 9000]
+    _say(f"decode long contexts {ctx}")
+    r = _decode_case(dev, ctx, 32, 8, seed=11)
+    check_attn(f64(r["o"]), r["ref"], "decode long")
+
+
+def _pool_workload(dev, w):
+    hkv = w.shape.num_kv_heads
+    kc = torch.empty((w.num_blocks, 256, hkv, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    wl.fill_normal_bf16_(kc, w.config_id, w.seed, 10)
+    wl.fill_normal_bf16_(vc, w.config_id, w.seed, 11)
+    return kc, vc
+
+
+def test_decode_0_6b_workload_full(dev):
+    w = wl.paged_decode_0_6b(seed=0)
+    _say("decode 0.6B workload: 64 sequences, contexts U[512, 8192]")
+    kc, vc = _pool_workload(dev, w)
+    q = to_dev(w.q(), dev)
+    o = pkv.attn_decode_paged(q, kc, vc, to_dev(w.context_lens, dev), to_dev(w.block_tables, dev))
+    torch.cuda.synchronize()
+    ref = oracle.attn_decode(bits(q), bits(kc).reshape(-1, 8, D), bits(vc).reshape(-1, 8, D), w.context_lens,
+                             w.block_tables, 16, 8)
+    check_attn(f64(o), ref, "decode 0.6B")
+
+
+def test_decode_8b_workload_sampled(dev):
+    w = wl.paged_decode_8b(seed=0)
+    _say("decode 8B workload: 256 sequences, contexts log-U[1024, 32768], shared prefix; 12 sampled")
+    kc, vc = _pool_workload(dev, w)
+    q = to_dev(w.q(), dev)
+    o = pkv.attn_decode_paged(q, kc, vc, to_dev(w.context_lens, dev), to_dev(w.block_tables, dev))
+    torch.cuda.synchronize()
+    r = np.random.default_rng(12)
+    seqs = list(r.choice(256, 8, replace=False)) + list(w.shared_seqs[:2]) + \
+        [int(np.argmax(w.context_lens)), int(np.argmin(w.context_lens))]
+    kch, vch, bt = gather_sequences(kc, vc, w.block_tables, seqs, w.context_lens)
+    ref = oracle.attn_decode(bits(q)[seqs], kch, vch, w.context_lens[seqs], bt, 32, 8)
+    check_attn(f64(o)[seqs], ref, "decode 8B")
+
+
+# ---------------------------------------------------------------------------
+# the tiny chain end to end, and decode == prefill row
+# ---------------------------------------------------------------------------
+
+def test_tiny_chain_end_to_end(dev, table_dev, table_host):
+    _say("tiny chain: qk_norm_rope -> store_kvcache -> prefill -> 4 decode steps")
+    w = wl.tiny_chain(seed=0)
+    s = w.shape
+    q0, k0, v0 = wl.qkv_views(s)
+    n = w.qkv.shape[0]
+    # GPU
+    kc = torch.zeros((w.num_blocks, 256, 8, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    qkv = to_dev(w.qkv, dev)
+    gq, gk = to_dev(w.gamma_q, dev), to_dev(w.gamma_k, dev)
+    qo, ko = pkv.qk_norm_rope(qkv[:, q0:k0].view(n, 16, D), qkv[:, k0:v0].view(n, 8, D),
+                              to_dev(w.positions, dev), gq, gk, table_dev, s.eps)
+    vv = qkv[:, v0:].view(n, 8, D)
+    pkv.store_kvcache(ko, vv, kc, vc, to_dev(w.slot_mapping, dev))
+    cu = to_dev(w.cu_seqlens, dev)
+    o = pkv.attn_prefill_varlen(qo, ko, vv, cu, cu, 300, 300)
+    # oracle
+    rq = oracle.rmsnorm_rope(w.qkv, 16, D, w.gamma_q, s.eps, w.positions, table_host, col_offset=q0)
+    rk = oracle.rmsnorm_rope(w.qkv, 8, D, w.gamma_k, s.eps, w.positions, table_host, col_offset=k0)
+    qb, kb = oracle.round_bf16(rq), oracle.round_bf16(rk)
+    vb = np.ascontiguousarray(w.qkv[:, v0:]).reshape(n, 8, D)
+    ekc = np.zeros((w.num_blocks * 256, 8, D), np.uint16)
+    evc = np.zeros_like(ekc)
+    oracle.store_kvcache(kb, vb, ekc, evc, w.slot_mapping)
+    ref = oracle.attn_prefill(qb, kb, vb, w.cu_seqlens, w.cu_seqlens, 16, 8)
+    torch.cuda.synchronize()
+    check_attn(f64(o), ref, "chain prefill")
+    # the page's integration check: cache rows at the written slots hold k' (within one bf16 ulp)
+    got_k = bits(kc).reshape(-1, 8, D)[w.slot_mapping]
+    check_ulp(got_k, rk, kb, "cached k'")
+    assert np.array_equal(bits(vc).reshape(-1, 8, D)[w.slot_mapping], vb)
+    bt = to_dev(w.block_tables, dev)
+    for st in w.decode_steps:
+        sq = to_dev(st.qkv, dev)
+        qd, kd = pkv.qk_norm_rope(sq[:, q0:k0].view(2, 16, D), sq[:, k0:v0].view(2, 8, D),
+                                  to_dev(st.positions, dev), gq, gk, table_dev, s.eps)
+        pkv.store_kvcache(kd, sq[:, v0:].view(2, 8, D), kc, vc, to_dev(st.slot_mapping, dev))
+        od = pkv.attn_decode_paged(qd, kc, vc, to_dev(st.context_lens, dev), bt)
+        rqd = oracle.round_bf16(oracle.rmsnorm_rope(st.qkv, 16, D, w.gamma_q, s.eps, st.positions, table_host,
+                                                    col_offset=q0))
+        rkd = oracle.round_bf16(oracle.rmsnorm_rope(st.qkv, 8, D, w.gamma_k, s.eps, st.positions, table_host,
+                                                    col_offset=k0))
+        oracle.store_kvcache(rkd, np.ascontiguousarray(st.qkv[:, v0:]).reshape(2, 8, D), ekc, evc, st.slot_mapping)
+        refd = oracle.attn_decode(rqd, ekc, evc, st.context_lens, w.block_tables, 16, 8)
+        torch.cuda.synchronize()
+        check_attn(f64(od), refd, f"chain decode pos {list(st.positions)}")
+
+
+def test_decode_row_equals_prefill_row(dev):
+    _say("decode at position i vs prefill row i (GPU vs GPU)")
+    lens = [41, 304, 777]
+    hq, hkv = 32, 8
+    o, _, inp = _prefill_case(dev, lens, lens, hq, hkv, seed=13, paged=True)
+    q, kc, vc, cuq, cuk, bt = inp
+    nb = kc.shape[0] // 256
+    last = cuq[1:] - 1
+    od = pkv.attn_decode_paged(to_dev(np.ascontiguousarray(q[last]), dev), to_dev(kc.reshape(nb, 256, hkv, D), dev),
+                               to_dev(vc.reshape(nb, 256, hkv, D), dev), to_dev(np.array(lens, np.int32), dev),
+                               to_dev(bt, dev))
+    torch.cuda.synchronize()
+    err = np.abs(f64(od) - f64(o)[last])
+    assert err.max() <= 2e-2, err.max()
