@@ -41,6 +41,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=24, help="decode sequences the oracle times")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -62,6 +64,17 @@ def main():
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            t0 = time.perf_counter()
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+        log(f"calibration copy: {src.numel() * 4 / 2**30:.0f} GiB read + written, {2 * src.numel() * 4 / dt / 1e9:.0f} GB/s")
+        del src, dst
 
     # ---------------- set-up (untimed) ----------------
     s8 = wl.QWEN3_8B

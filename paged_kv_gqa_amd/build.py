@@ -36,8 +36,8 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra, objdir: str = OBJDIR) -> str:
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -49,19 +49,19 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra_flags=None, jobs: int = 8) -> str:
-    """Compile every HIP source for gfx950 and link libpkv.so; returns its path."""
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(extra_flags=None, jobs: int = 8, out: str = LIB, objdir: str = OBJDIR) -> str:
+    """Compile every HIP source for gfx950 and link libpkv.so (or `out`); returns its path."""
+    os.makedirs(objdir, exist_ok=True)
     extra = list(extra_flags or [])
     with cf.ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, extra, objdir), SOURCES))
+    tmp = out + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

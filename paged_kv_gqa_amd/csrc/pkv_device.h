@@ -32,11 +32,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ u32x4 ldg128(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void stg128(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
-// Non-temporal 128-bit global load: streamed data that is read exactly once.
-__device__ __forceinline__ u32x4 ldg128_stream(const void* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
