@@ -20,11 +20,20 @@
 //     already the B operand of the PV product.
 //   * A workgroup (4 waves, 32 query rows each) owns one kv head and the
 //     query heads of its GQA group that share it, so each K/V tile staged in
-//     LDS feeds 128 query rows.  K is kept row-major in LDS, V transposed
-//     (the PV contraction runs over keys), both padded against bank conflicts.
-//   * The next tile is loaded into registers while the current one is
-//     computed.  Tiles of 64 keys never straddle a 256-token block, so the
-//     paged loader does one block-table lookup per tile.
+//     LDS feeds 128 query rows.  K and V are both kept row-major in LDS
+//     (plain 16-byte copies, padded rows: no bank conflicts); the PV product
+//     needs V transposed, which the gfx950 transposing LDS read
+//     (ds_read_b64_tr_b16) delivers: lane j of a 16-lane group addresses key
+//     j/4, dims 4*(j%4) of a 4-key x 16-dim tile and receives its own dim
+//     across the 4 keys.
+//   * Double-buffered LDS (one barrier per tile); the tile after next is
+//     loaded into registers while the current one is computed.  Tiles of 64
+//     keys never straddle a 256-token block, so the paged loader does one
+//     block-table lookup per tile.  Loads are issued on every path (rows past
+//     the last key are clamped) so the compiler's wait counts stay exact.
+//   * Softmax: row max on raw scores, scale folded into one FMA ahead of the
+//     hardware exp2; the running max is a lazy reference that moves only when
+//     a row grows by more than 2^8, so the O rescale is skipped on most tiles.
 //   * Causal tile skipping: a wave stops at the tile holding its last visible
 //     key; only tiles that cross the diagonal (or the sequence end) are masked.
 //   * Work order: longest query blocks first inside each (sequence, kv head),
@@ -35,12 +44,16 @@
 namespace pkv {
 
 namespace {
+typedef __attribute__((address_space(3))) bf16x4* lds_ptr_t;
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
 constexpr int kKT = 64;                    // keys per tile
-constexpr int kKPitch = kHeadDim * 2 + 16;  // bytes per K row in LDS
-constexpr int kVPitch = kKT * 2 + 8;        // bytes per transposed V row in LDS
+constexpr int kKPitch = kHeadDim * 2 + 16;  // bytes per K row in LDS (row-major)
+constexpr int kVPitch = kHeadDim * 2 + 64;  // bytes per V row in LDS (row-major, read transposed)
+constexpr int kKTileBytes = kKT * kKPitch;
+constexpr int kVTileBytes = kKT * kVPitch;
+constexpr float kLazyLog2 = 8.0f;           // the lazy reference max moves when a row grows by > 2^8
 }  // namespace
 
 template <int GW, bool PAGED>
@@ -48,8 +61,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
                                                               int32_t head_groups) {
     constexpr int kPosSub = kWaves / GW;                // position sub-blocks per workgroup
     constexpr int kBM = kRowsPerWave * kPosSub;         // query positions per workgroup
-    __shared__ __attribute__((aligned(16))) unsigned char k_lds[kKT * kKPitch];
-    __shared__ __attribute__((aligned(16))) unsigned char v_lds[kHeadDim * kVPitch];
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds[2 * kKTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds[2 * kVTileBytes];
 
     const int work = xcd_remap(blockIdx.x, n_work);
     if (work >= n_work) return;
@@ -99,15 +112,28 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-    float m_run = -INFINITY, l_part = 0.f;
+    float m_run = -INFINITY, l_part = 0.f;      // running reference max (raw units), partial sum
+    const float lazy_raw = kLazyLog2 / a.scale_log2;
 
-    // ---- tile loader: K as 4 x 16 B per thread (row-major), V as 4 keys x 8 dims per thread.
+    // ---- tile loader.  Thread tid moves 16-byte piece tid%16 of rows tid/16 + 16*i
+    // (i < 4) of the 64-row K and V tiles.  Row offsets are loop-invariant; every
+    // load is issued on every path (rows past the last key are clamped onto it), so
+    // the compiler's wait counts stay exact.
     const int64_t krs = a.k_row_stride, vrs = a.v_row_stride;
     const uint16_t* kbase = (const uint16_t*)a.k + (int64_t)g * kHeadDim;
     const uint16_t* vbase = (const uint16_t*)a.v + (int64_t)g * kHeadDim;
     const int32_t* bt = PAGED ? a.block_table + (int64_t)b * a.max_blocks : nullptr;
-    auto tile_row0 = [&](int j0, bool& ok) -> int64_t {
-        // cache / array row of key j0 (tiles never straddle a 256-token block)
+    const int lrow = tid >> 4, piece = tid & 15;
+    int64_t koff[4], voff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        koff[i] = (int64_t)(lrow + 16 * i) * krs + piece * 8;
+        voff[i] = (int64_t)(lrow + 16 * i) * vrs + piece * 8;
+    }
+    // First cache/array row of tile t and whether its block id is usable (tiles
+    // never straddle a 256-token block).
+    auto tile_row0 = [&](int t, bool& ok) -> int64_t {
+        const int j0 = t * kKT;
         if (PAGED) {
             const int bi = j0 / kBlockSize;
             const int32_t blk = bi < a.max_blocks ? bt[bi] : -1;
@@ -120,110 +146,126 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
     };
     u32x4 kst[4], vst[4];
     auto load_tile = [&](int t) {
-        const int j0 = t * kKT;
         bool ok;
-        const int64_t r0 = tile_row0(j0, ok);
+        const int64_t r0 = tile_row0(t, ok);
+        const int last = Lk - 1 - t * kKT;              // last valid row of this tile (>= 0)
+        if (ok && last >= kKT - 1) {
+            const uint16_t* kp = kbase + r0 * krs;
+            const uint16_t* vp = vbase + r0 * vrs;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + kThreads * i;             // 16-byte chunk of the 64 x 256 B K tile
-            const int key = c >> 4, piece = c & 15;
-            const bool in = ok && (j0 + key) < Lk;
-            kst[i] = in ? ldg128(kbase + (r0 + key) * krs + piece * 8) : u32x4{0u, 0u, 0u, 0u};
-        }
-        const int kq = tid >> 4, dg = tid & 15;
+            for (int i = 0; i < 4; ++i) kst[i] = ldg128(kp + koff[i]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = 4 * kq + r;
-            const bool in = ok && (j0 + key) < Lk;
-            vst[r] = in ? ldg128(vbase + (r0 + key) * vrs + dg * 8) : u32x4{0u, 0u, 0u, 0u};
+            for (int i = 0; i < 4; ++i) vst[i] = ldg128(vp + voff[i]);
+        } else {
+            // partial or unusable tile: clamp rows onto valid memory, zero V at store time
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = r0 + (ok ? min(lrow + 16 * i, last) : 0);
+                kst[i] = ldg128(kbase + row * krs + piece * 8);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = r0 + (ok ? min(lrow + 16 * i, last) : 0);
+                vst[i] = ldg128(vbase + row * vrs + piece * 8);
+            }
         }
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](int t, unsigned char* kb, unsigned char* vb) {
+        bool ok;
+        (void)tile_row0(t, ok);
+        const int last = Lk - 1 - t * kKT;
+        if (!ok || last < kKT - 1) {
+            // V rows of keys past the end (or of an unusable block) become zeros, so
+            // whatever those cache slots hold cannot reach the output through P V.
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (!ok || lrow + 16 * i > last) vst[i] = u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int c = tid + kThreads * i;
-            const int key = c >> 4, piece = c & 15;
-            *reinterpret_cast<u32x4*>(k_lds + key * kKPitch + piece * 16) = kst[i];
-        }
-        // transpose 4 keys x 8 dims -> 8 rows (dims) of 4 keys
-        const int kq = tid >> 4, dg = tid & 15;
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-            // dims 8dg + 2e2 (low halves) and 8dg + 2e2 + 1 (high halves)
-            const uint32_t a0 = vst[0][e2], a1 = vst[1][e2], a2 = vst[2][e2], a3 = vst[3][e2];
-            u32x2 lo, hi;
-            lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);   // keys 0,1 of the even dim
-            lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);   // keys 2,3
-            hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // keys 0,1 of the odd dim
-            hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-            const int d0 = 8 * dg + 2 * e2;
-            *reinterpret_cast<u32x2*>(v_lds + d0 * kVPitch + kq * 8) = lo;
-            *reinterpret_cast<u32x2*>(v_lds + (d0 + 1) * kVPitch + kq * 8) = hi;
+            *reinterpret_cast<u32x4*>(kb + (lrow + 16 * i) * kKPitch + piece * 16) = kst[i];
+            *reinterpret_cast<u32x4*>(vb + (lrow + 16 * i) * kVPitch + piece * 16) = vst[i];
         }
     };
 
     const int h32 = lane >> 5;  // which half of the k-slots this lane feeds
+    // Double-buffered LDS tiles: one barrier per tile.  Tile t is computed from buffer
+    // t&1 while tile t+1 (loaded into registers one iteration earlier) is stored into
+    // the other buffer; tile t+2 is loaded after the barrier.
     load_tile(0);
+    store_tile(0, k_lds, v_lds);
+    if (1 < n_tiles) load_tile(1);
+    __syncthreads();
     for (int t = 0; t < n_tiles; ++t) {
-        __syncthreads();          // all waves are done with the previous tile
-        store_tile();
-        __syncthreads();
-        if (t + 1 < n_tiles) load_tile(t + 1);
-        if (t >= wave_tiles) continue;   // past this wave's last visible key
-
-        const int j0 = t * kKT;
+        unsigned char* kb = k_lds + (t & 1) * kKTileBytes;
+        unsigned char* vb = v_lds + (t & 1) * kVTileBytes;
+        if (t < wave_tiles) {   // this wave still has visible keys in tile t
+          const int j0 = t * kKT;
         bool ok;
-        (void)tile_row0(j0, ok);
+        (void)tile_row0(t, ok);
         // ---- S^T = K Q^T for two 32-key halves
         f32x16 s[2];
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kh][r] = 0.f;
-            const unsigned char* kr = k_lds + (32 * kh + (lane & 31)) * kKPitch + 16 * h32;
+            const unsigned char* kr = kb + (32 * kh + (lane & 31)) * kKPitch + 16 * h32;
 #pragma unroll
             for (int st = 0; st < 8; ++st) {
                 const bf16x8 av = *reinterpret_cast<const bf16x8*>(kr + 32 * st);
                 s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[st], s[kh], 0, 0, 0);
             }
         }
-        // s[kh][r] = score of key j0 + 32kh + 8(r/4) + 4*h32 + r%4 for query qi.
+        // s[kh][r] = raw score of key j0 + 32kh + 8(r/4) + 4*h32 + r%4 for query qi.
         const bool need_mask = !ok || (j0 + kKT - 1 > off + wp0) || (j0 + kKT > Lk);
+        if (need_mask) {
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kp = j0 + 32 * kh + 8 * (r >> 2) + 4 * h32 + (r & 3);
+                    s[kh][r] = (!ok || kp > qpos || kp >= Lk) ? -INFINITY : s[kh][r];
+                }
+        }
         float tmax = -INFINITY;
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float v = s[kh][r] * a.scale_log2;
-                if (need_mask) {
-                    const int kp = j0 + 32 * kh + 8 * (r >> 2) + 4 * h32 + (r & 3);
-                    v = (!ok || kp > qpos || kp >= Lk) ? -INFINITY : v;
-                }
-                s[kh][r] = v;
-                tmax = fmaxf(tmax, v);
-            }
+            for (int r = 0; r < 16; r += 2) tmax = __builtin_fmaxf(__builtin_fmaxf(tmax, s[kh][r]), s[kh][r + 1]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float mn = fmaxf(m_run, tmax);
-        const float ref = mn == -INFINITY ? 0.f : mn;
-        const float alpha = exp2f(m_run - ref);
-        m_run = mn;
+        // Lazy reference max (raw score units): it moves only when a row's max grows
+        // by more than 2^kLazyLog2 in the exponent, so the weights stay <= 256 and the
+        // O rescale is skipped on most tiles.  Exact: O and l share the reference.
+        const bool grow = tmax > m_run + lazy_raw;
+        if (__any(grow)) {
+            const float mn = grow ? tmax : m_run;
+            const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - mn) * a.scale_log2);
+            m_run = mn;
+            l_part *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        }
+        const float moff = m_run == -INFINITY ? 0.f : -m_run * a.scale_log2;
         float psum = 0.f;
         uint32_t pk[2][8];
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                const float e0 = exp2f(s[kh][r] - ref), e1 = exp2f(s[kh][r + 1] - ref);
+                const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kh][r], a.scale_log2, moff));
+                const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kh][r + 1], a.scale_log2, moff));
                 psum += e0 + e1;
                 pk[kh][r >> 1] = pack_bf16x2(e0, e1);
             }
-        l_part = l_part * alpha + psum;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        l_part += psum;
 
         // ---- O^T += V^T P^T: per 16-key step (kh, v) the B operand is registers 8v..8v+7 of s[kh].
+        // The A operand (V^T: row d = lane%32, 8 keys) comes from row-major V with two
+        // transposing LDS reads: lane j of a 16-lane group addresses key j/4, dims 4*(j%4)
+        // of a 4-key x 16-dim tile and receives its own dim across the 4 keys.
+        const int grp16 = lane >> 4, j16 = lane & 15;
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -233,14 +275,19 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
                 const int kcol = 32 * kh + 16 * v + 4 * h32;   // first key of this lane's k-slots
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt) {
-                    const unsigned char* vr = v_lds + (32 * dt + (lane & 31)) * kVPitch + 2 * kcol;
-                    const u32x2 x0 = *reinterpret_cast<const u32x2*>(vr);
-                    const u32x2 x1 = *reinterpret_cast<const u32x2*>(vr + 16);
-                    u32x4 aw = {x0[0], x0[1], x1[0], x1[1]};
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, aw), bv, oacc[dt],
-                                                                       0, 0, 0);
+                    const int d0 = 32 * dt + 16 * (grp16 & 1) + 4 * (j16 & 3);
+                    lds_ptr_t p0 = (lds_ptr_t)(vb + (kcol + (j16 >> 2)) * kVPitch + 2 * d0);
+                    lds_ptr_t p1 = (lds_ptr_t)(vb + (kcol + 8 + (j16 >> 2)) * kVPitch + 2 * d0);
+                    const bf16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p0);
+                    const bf16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p1);
+                    const bf16x8 av = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, oacc[dt], 0, 0, 0);
                 }
             }
+        }
+        if (t + 1 < n_tiles) store_tile(t + 1, k_lds + ((t + 1) & 1) * kKTileBytes, v_lds + ((t + 1) & 1) * kVTileBytes);
+        __syncthreads();
+        if (t + 2 < n_tiles) load_tile(t + 2);
     }
 
     // ---- normalise and store: lane holds O^T[d][qi] for d = 32dt + 8(r/4) + 4*h32 + r%4.
