@@ -2,11 +2,14 @@
 
 One step = one pass of the whole hot path over both 8B workloads:
   prefill phase  (16 sequences x 4096 tokens, first 2048 cached in shared blocks):
-      qk_norm_rope over 32768 new tokens -> store_kvcache of their K/V ->
-      paged causal prefill (2048 queries per sequence over 4096 keys);
+      QK-Norm + RoPE over 32768 new tokens with their K/V scattered into the
+      cache in the same pass -> paged causal prefill (2048 queries per sequence
+      over 4096 keys);
   decode phase   (256 sequences, contexts log-uniform in [1024, 32768], 64 of them
                   sharing an 8-block prefix):
-      qk_norm_rope over 256 tokens -> store_kvcache -> paged decode.
+      QK-Norm + RoPE + scatter of the 256 new tokens -> paged decode.
+The unfused pair (qk_norm_rope, then store_kvcache) is timed separately after
+the step loop and reported under "kernels".
 
 Inputs are synthetic and seeded (``workloads``), resident in HBM before timing.
 Prints one JSON line.  ``value`` is the paged-decode attention throughput in GB/s
@@ -62,7 +65,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seqs", type=int, default=24, help="decode sequences the oracle times")
+    ap.add_argument("--cpu-seqs", type=int, default=256, help="decode sequences the oracle times")
+    ap.add_argument("--cpu-prefill-rows", type=int, default=131072, help="prefill (token, head) rows the oracle times")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -146,31 +150,42 @@ def main():
     kv_d = qkv_d[:, k0:v0].view(B, s8.num_kv_heads, D)
     vv_d = qkv_d[:, v0:].view(B, s8.num_kv_heads, D)
     stream = torch.cuda.current_stream()
-    names = ["norm_rope_p", "store_p", "prefill", "norm_rope_d", "store_d", "decode"]
+    names = ["norm_rope_store_p", "prefill", "norm_rope_store_d", "decode"]
 
     def step(ev=None):
+        """QK-Norm + RoPE + cache scatter (one fused pass) then attention, for both phases."""
         def mark(i):
             if ev is not None:
                 ev[i].record(stream)
         mark(0)
-        pkv.qk_norm_rope(qv_p, kv_p, pos_p, gq_p, gk_p, table, s8.eps, q_out=qo_p, k_out=ko_p)
+        pkv.qk_norm_rope_store(qv_p, kv_p, vv_p, pos_p, gq_p, gk_p, table, kc_p, vc_p, slot_p, s8.eps, q_out=qo_p)
         mark(1)
-        pkv.store_kvcache(ko_p, vv_p, kc_p, vc_p, slot_p)
-        mark(2)
         pkv.attn_prefill_varlen(qo_p, kc_p, vc_p, cuq_p, cuk_p, wp.suffix_len, wp.total_len, block_table=bt_p,
                                 out=o_p)
+        mark(2)
+        pkv.qk_norm_rope_store(qv_d, kv_d, vv_d, pos_d, gq_d, gk_d, table, kc_d, vc_d, slot_d, s8.eps, q_out=qo_d)
         mark(3)
-        pkv.qk_norm_rope(qv_d, kv_d, pos_d, gq_d, gk_d, table, s8.eps, q_out=qo_d, k_out=ko_d)
-        mark(4)
-        pkv.store_kvcache(ko_d, vv_d, kc_d, vc_d, slot_d)
-        mark(5)
         pkv.attn_decode_paged(qo_d, kc_d, vc_d, cl_d, bt_d, out=o_d, workspace=ws)
-        mark(6)
+        mark(4)
+
+    unfused_names = ["norm_rope_p", "store_p", "norm_rope_d", "store_d"]
+
+    def unfused(ev):
+        """The same first steps as two separate calls each (QK-Norm + RoPE, then the scatter)."""
+        ev[0].record(stream)
+        pkv.qk_norm_rope(qv_p, kv_p, pos_p, gq_p, gk_p, table, s8.eps, q_out=qo_p, k_out=ko_p)
+        ev[1].record(stream)
+        pkv.store_kvcache(ko_p, vv_p, kc_p, vc_p, slot_p)
+        ev[2].record(stream)
+        pkv.qk_norm_rope(qv_d, kv_d, pos_d, gq_d, gk_d, table, s8.eps, q_out=qo_d, k_out=ko_d)
+        ev[3].record(stream)
+        pkv.store_kvcache(ko_d, vv_d, kc_d, vc_d, slot_d)
+        ev[4].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -181,27 +196,48 @@ def main():
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in events])) for j, n in enumerate(names)}
     ms_step = wall * 1e3 / args.steps
 
+    # the unfused first steps, timed after the step loop (not part of ms_per_step)
+    for _ in range(args.warmup):
+        unfused([torch.cuda.Event(enable_timing=True) for _ in range(5)])
+    uev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        unfused(uev[i])
+    torch.cuda.synchronize()
+    per.update({n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in uev])) for j, n in enumerate(unfused_names)})
+
     dec_bytes = wd.algorithmic_bytes(unique=True)
     dec_gbs = dec_bytes / (per["decode"] * 1e-3) / 1e9
     pre_tflops = wp.flops / (per["prefill"] * 1e-3) / 1e12
     store_bytes = wp.store_bytes
-    norm_bytes = Tq * ((s8.num_q_heads + s8.num_kv_heads) * D * 2 * 2 + 8 + 512)
+    hq8, hkv8 = s8.num_q_heads, s8.num_kv_heads
+    # per token: q, k read + q', k' written; positions (8 B) and one table row (512 B) read
+    norm_bytes = Tq * ((hq8 + hkv8) * D * 2 * 2 + 8 + 512)
+    # fused, per token: q, k, v read + q', k', v written; position, slot id and table row read
+    fused_bytes = Tq * ((hq8 + 2 * hkv8) * D * 2 * 2 + 8 + 4 + 512)
+
+    def gbs(nbytes, ms):
+        return nbytes / (ms * 1e-3) / 1e9
+
     kernels = {
         "attn_decode_paged": {"ms": per["decode"], "GB/s": dec_gbs, "bytes": dec_bytes,
                               "logical_bytes": wd.algorithmic_bytes(unique=False)},
         "attn_prefill_varlen": {"ms": per["prefill"], "TFLOP/s": pre_tflops, "flop": wp.flops},
-        "store_kvcache_prefill": {"ms": per["store_p"], "GB/s": store_bytes / (per["store_p"] * 1e-3) / 1e9,
-                                  "bytes": store_bytes},
-        "qk_norm_rope_prefill": {"ms": per["norm_rope_p"], "GB/s": norm_bytes / (per["norm_rope_p"] * 1e-3) / 1e9,
-                                 "bytes": norm_bytes},
-        "qk_norm_rope_decode": {"ms": per["norm_rope_d"]},
-        "store_kvcache_decode": {"ms": per["store_d"]},
+        "qk_norm_rope_store_prefill": {"ms": per["norm_rope_store_p"],
+                                       "GB/s": gbs(fused_bytes, per["norm_rope_store_p"]), "bytes": fused_bytes},
+        "qk_norm_rope_store_decode": {"ms": per["norm_rope_store_d"]},
+        "unfused_store_kvcache_prefill": {"ms": per["store_p"], "GB/s": gbs(store_bytes, per["store_p"]),
+                                          "bytes": store_bytes},
+        "unfused_qk_norm_rope_prefill": {"ms": per["norm_rope_p"], "GB/s": gbs(norm_bytes, per["norm_rope_p"]),
+                                         "bytes": norm_bytes},
+        "unfused_qk_norm_rope_decode": {"ms": per["norm_rope_d"]},
+        "unfused_store_kvcache_decode": {"ms": per["store_d"]},
     }
     log(json.dumps(kernels))
 
-    cpu = None
+    cpu = cpu_pre = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, wd, kc_d, vc_d, qo_d, log)
+        cpu_pre = cpu_baseline_prefill(args, wp, kc_p, vc_p, qo_p, log)
 
     out = {
         "metric": METRIC,
@@ -234,12 +270,17 @@ def main():
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "cpu_baseline": cpu,
+        "cpu_baseline_prefill": cpu_pre,
     }
     print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(args, wd, kc_d, vc_d, q_d, log):
-    """The oracle's paged decode on a bounded sample of the same workload, on the host cores."""
+    """The oracle's paged decode over the decode workload's sequences, on the host cores.
+
+    Sequences are copied back and run in groups of 32 so host memory stays bounded;
+    only the oracle calls are timed.  Units: GB/s of the same algorithmic bytes.
+    """
     import torch
 
     import oracle
@@ -248,30 +289,62 @@ def cpu_baseline(args, wd, kc_d, vc_d, q_d, log):
     def bits(t):
         return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
-    def gather_sequences(k_cache, v_cache, block_table, seqs, context_lens):
-        rows = [[int(x) for x in block_table[b, :-(-int(context_lens[b]) // 256)]] for b in seqs]
+    def gather_sequences(seqs):
+        rows = [[int(x) for x in wd.block_tables[b, :-(-int(wd.context_lens[b]) // 256)]] for b in seqs]
         uniq = sorted({p for r in rows for p in r})
         where = {p: i for i, p in enumerate(uniq)}
-        idx = torch.tensor(uniq, dtype=torch.int64, device=k_cache.device)
-        hkv = k_cache.shape[2]
-        kc = bits(k_cache.index_select(0, idx)).reshape(len(uniq) * 256, hkv, 128)
-        vc = bits(v_cache.index_select(0, idx)).reshape(len(uniq) * 256, hkv, 128)
-        return kc, vc, wl.pad_block_tables([[where[p] for p in r] for r in rows], block_table.shape[1])
+        idx = torch.tensor(uniq, dtype=torch.int64, device=kc_d.device)
+        hkv = kc_d.shape[2]
+        kc = bits(kc_d.index_select(0, idx)).reshape(len(uniq) * 256, hkv, 128)
+        vc = bits(vc_d.index_select(0, idx)).reshape(len(uniq) * 256, hkv, 128)
+        return kc, vc, wl.pad_block_tables([[where[p] for p in r] for r in rows], wd.block_tables.shape[1])
 
-    rng = np.random.default_rng(args.seed + 100)
-    seqs = sorted(rng.choice(wd.batch, size=min(args.cpu_seqs, wd.batch), replace=False).tolist())
-    kc, vc, bt = gather_sequences(kc_d, vc_d, wd.block_tables, seqs, wd.context_lens)
-    q = bits(q_d)[seqs]
-    cl = wd.context_lens[seqs]
-    oracle.attn_decode(q[:1], kc, vc, cl[:1], bt[:1], 32, 8)       # warm the library
+    n = min(args.cpu_seqs, wd.batch)
+    seqs_all = list(range(n))
+    qh = bits(q_d)
+    hq, hkv = wd.shape.num_q_heads, wd.shape.num_kv_heads
+    total, nbytes, toks = 0.0, 0, 0
+    for s0 in range(0, n, 32):
+        seqs = seqs_all[s0:s0 + 32]
+        kc, vc, bt = gather_sequences(seqs)
+        cl = wd.context_lens[seqs]
+        t0 = time.perf_counter()
+        oracle.attn_decode(qh[seqs], kc, vc, cl, bt, hq, hkv)
+        total += time.perf_counter() - t0
+        toks += int(np.sum(cl.astype(np.int64)))
+        nbytes += int(np.sum(cl.astype(np.int64))) * hkv * 128 * 2 * 2 + len(seqs) * hq * 128 * 2 * 2
+        del kc, vc
+    log(f"cpu baseline: {n} sequences, {nbytes / 1e9:.3f} GB in {total:.2f} s")
+    return {"value": round(nbytes / total / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"paged decode of {n} of the {wd.batch} sequences ({toks} context tokens, {hq}/{hkv} heads), "
+                      f"fp64 C oracle with OpenMP, {total:.2f} s of oracle time (K/V read per sequence, "
+                      f"shared prefix counted per sequence)"}
+
+
+def cpu_baseline_prefill(args, wp, kc_p, vc_p, q_p, log):
+    """The oracle's paged prefill on a sample of (token, head) rows of the prefill workload."""
+    import torch
+
+    import oracle
+
+    def bits(t):
+        return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    rng = np.random.default_rng(args.seed + 200)
+    nrows = args.cpu_prefill_rows
+    t = rng.integers(0, wp.num_q_tokens, nrows)
+    h = rng.integers(0, wp.shape.num_q_heads, nrows)
+    rows = np.stack([t, h], 1)
+    kc, vc = bits(kc_p).reshape(-1, 8, 128), bits(vc_p).reshape(-1, 8, 128)
+    qh = bits(q_p)
     t0 = time.perf_counter()
-    oracle.attn_decode(q, kc, vc, cl, bt, 32, 8)
+    oracle.attn_prefill(qh, kc, vc, wp.cu_seqlens_q, wp.cu_seqlens_k, wp.shape.num_q_heads, wp.shape.num_kv_heads,
+                        block_table=wp.block_tables, rows=rows)
     dt = time.perf_counter() - t0
-    nbytes = int(np.sum(cl.astype(np.int64))) * 8 * 128 * 2 * 2 + len(seqs) * 32 * 128 * 2 * 2
-    log(f"cpu baseline: {len(seqs)} sequences, {nbytes / 1e9:.3f} GB in {dt:.2f} s")
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"paged decode of {len(seqs)} of the {wd.batch} sequences ({int(np.sum(cl))} context tokens, "
-                      f"32 q heads), fp64 C oracle with OpenMP, {dt:.2f} s"}
+    flop = float(np.sum(4 * 128 * (wp.positions[t] + 1)))
+    log(f"cpu prefill baseline: {nrows} rows, {flop / 1e9:.2f} GFLOP in {dt:.2f} s")
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{nrows} random (token, head) rows of the prefix-hit prefill, fp64 C oracle, {dt:.2f} s"}
 
 
 if __name__ == "__main__":

@@ -9,7 +9,9 @@
  *   pkv_attn_prefill_varlen  varlen causal GQA prefill (fresh K/V or paged)
  *   pkv_attn_decode_paged    single-token paged decode
  *
- * plus pkv_rope_cache_build, which fills the cos/sin table once at set-up.
+ * plus pkv_rope_cache_build, which fills the cos/sin table once at set-up, and
+ * pkv_qk_norm_rope_store, the first two steps in one pass (rotated k and v go
+ * straight to their cache rows).
  *
  * Conventions for every entry point
  *   - Every pointer argument is a DEVICE pointer owned by the caller, unless
@@ -130,6 +132,35 @@ PKV_API int pkv_qk_norm_rope(const void* q, int64_t q_row_stride, const void* k,
 PKV_API int pkv_store_kvcache(const void* key, int64_t key_row_stride, const void* value, int64_t value_row_stride,
                       void* k_cache, void* v_cache, int64_t num_slots, const int32_t* slot_mapping,
                       int32_t n_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t elem_bytes, void* stream);
+
+/*
+ * pkv_qk_norm_rope_store -- pkv_qk_norm_rope and pkv_store_kvcache in one
+ * pass, [Ops] s3, s7.1, s8; [Attn17] s4, s5.1.  Per token t the rotated key
+ * heads are written straight into k_cache row slot_mapping[t] and the value
+ * heads into v_cache row slot_mapping[t]; the rotated query heads go to q_out.
+ * Every value written is bit-identical to calling pkv_qk_norm_rope and then
+ * pkv_store_kvcache(k_out, ..., v, ...) with the same arguments.
+ *
+ *   q, k, q_out, positions, norm weights, cos_sin_cache, max_position:
+ *                   as for pkv_qk_norm_rope (q_out may alias q exactly).
+ *   v, v_row_stride value rows of num_kv_heads*head_dim bf16 (e.g. the v
+ *                   columns of the qkv rows); read only.
+ *   k_out           optional contiguous [n_tokens][num_kv_heads][head_dim] copy
+ *                   of the rotated keys (NULL: not written).  It may alias k
+ *                   exactly when k is contiguous.
+ *   k_cache, v_cache, num_slots, slot_mapping:
+ *                   as for pkv_store_kvcache with elem_bytes 2; a slot outside
+ *                   [0, num_slots), -1 included, writes no cache row (q_out and
+ *                   k_out are still written).  The caches must not overlap
+ *                   q, k, v or the outputs.
+ */
+PKV_API int pkv_qk_norm_rope_store(const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride,
+                                   const void* v, int64_t v_row_stride, void* q_out, void* k_out, void* k_cache,
+                                   void* v_cache, int64_t num_slots, const int32_t* slot_mapping,
+                                   const int64_t* positions, int32_t n_tokens, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, const void* q_norm_weight,
+                                   const void* k_norm_weight, float eps, const float* cos_sin_cache,
+                                   int32_t max_position, void* stream);
 
 /*
  * pkv_attn_prefill_varlen -- causal GQA attention over a packed batch of

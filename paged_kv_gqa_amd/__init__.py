@@ -11,6 +11,8 @@ Entry points mirror the calls the attention pages describe
 * ``rope_cache_build``   -- the fp32 cos/sin table, once
 * ``qk_norm_rope``       -- q_norm / k_norm then rotary_emb(positions, q, k)
 * ``store_kvcache``      -- store_kvcache(key, value, k_cache, v_cache, slot_mapping)
+* ``qk_norm_rope_store`` -- the two steps above in one pass (rotated k and v go
+                            straight to their cache rows)
 * ``attn_prefill_varlen``-- flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k,
                             max_seqlen_q, max_seqlen_k, softmax_scale, causal, block_table)
 * ``attn_decode_paged``  -- flash_attn_with_kvcache(q, k_cache, v_cache, cache_seqlens,
@@ -31,8 +33,8 @@ PKV_OK = 0
 _STATUS = {-1: "invalid argument", -2: "unsupported", -3: "launch failed", -4: "workspace"}
 
 #: every symbol include/pkv.h declares
-EXPORTED = ("pkv_last_error", "pkv_version", "pkv_rope_cache_build", "pkv_qk_norm_rope", "pkv_store_kvcache",
-            "pkv_attn_prefill_varlen", "pkv_attn_decode_workspace_bytes", "pkv_attn_decode_paged")
+EXPORTED = ("pkv_last_error", "pkv_version", "pkv_rope_cache_build", "pkv_qk_norm_rope",
+            "pkv_qk_norm_rope_store", "pkv_store_kvcache", "pkv_attn_prefill_varlen", "pkv_attn_decode_workspace_bytes", "pkv_attn_decode_paged")
 
 _lib = None
 
@@ -61,6 +63,9 @@ def load_library(path: str = LIB_PATH):
     lib.pkv_rope_cache_build.restype = ctypes.c_int
     lib.pkv_qk_norm_rope.argtypes = [P, I64, P, I64, P, P, P, I32, I32, I32, I32, P, P, F32, P, I32, P]
     lib.pkv_qk_norm_rope.restype = ctypes.c_int
+    lib.pkv_qk_norm_rope_store.argtypes = [P, I64, P, I64, P, I64, P, P, P, P, I64, P, P, I32, I32, I32, I32, P,
+                                           P, F32, P, I32, P]
+    lib.pkv_qk_norm_rope_store.restype = ctypes.c_int
     lib.pkv_store_kvcache.argtypes = [P, I64, P, I64, P, P, I64, P, I32, I32, I32, I32, P]
     lib.pkv_store_kvcache.restype = ctypes.c_int
     lib.pkv_attn_prefill_varlen.argtypes = [P, I64, P, I64, P, I64, P, P, P, I32, I32, I32, I32, I32, I32, I32,
@@ -153,6 +158,41 @@ def qk_norm_rope(q, k, positions, q_norm_weight, k_norm_weight, cos_sin_cache, e
                                 HEAD_DIM, _ptr(q_norm_weight), _ptr(k_norm_weight), float(eps),
                                 _ptr(cos_sin_cache), cos_sin_cache.shape[0], _stream(stream)))
     return q_out, k_out
+
+
+def qk_norm_rope_store(q, k, v, positions, q_norm_weight, k_norm_weight, cos_sin_cache, k_cache, v_cache,
+                       slot_mapping, eps: float = 1.0e-6, q_out=None, k_out=None, stream=None):
+    """QK-Norm + RoPE with the cache scatter fused in.  q: [N, Hq, 128], k, v: [N, Hkv, 128]
+    bf16 views (row-strided allowed); caches [num_blocks, 256, Hkv, 128]; slot_mapping [N] int32.
+
+    The rotated keys and the values land in their cache rows; returns q_out (contiguous,
+    allocated if not given; q_out=q runs in place).  k_out, if given, also receives the
+    rotated keys.
+    """
+    import torch
+    lib = load_library()
+    n, hq, hkv = q.shape[0], q.shape[1], k.shape[1]
+    qs, ks, vs = _rows(q, hq, "q"), _rows(k, hkv, "k"), _rows(v, hkv, "v")
+    if k.shape[0] != n or v.shape[0] != n or positions.shape[0] != n or slot_mapping.numel() != n:
+        raise ValueError("q, k, v, positions and slot_mapping must have the same number of tokens")
+    if positions.dtype != torch.int64 or not positions.is_contiguous():
+        raise TypeError("positions must be a contiguous int64 tensor")
+    _i32(slot_mapping, "slot_mapping")
+    D = hkv * HEAD_DIM
+    for c in (k_cache, v_cache):
+        if c.dtype != torch.bfloat16 or not c.is_contiguous() or c.dim() != 4 or c.stride(1) != D:
+            raise ValueError("caches must be contiguous bf16 [num_blocks, block_size, Hkv, 128]")
+    if q_out is None:
+        q_out = torch.empty((n, hq, HEAD_DIM), dtype=torch.bfloat16, device=q.device)
+    if not q_out.is_contiguous() or (k_out is not None and not k_out.is_contiguous()):
+        raise ValueError("q_out and k_out must be contiguous")
+    _check("pkv_qk_norm_rope_store",
+           lib.pkv_qk_norm_rope_store(_ptr(q), qs, _ptr(k), ks, _ptr(v), vs, _ptr(q_out), _ptr(k_out),
+                                      _ptr(k_cache), _ptr(v_cache), k_cache.numel() // D, _ptr(slot_mapping),
+                                      _ptr(positions), n, hq, hkv, HEAD_DIM, _ptr(q_norm_weight),
+                                      _ptr(k_norm_weight), float(eps), _ptr(cos_sin_cache),
+                                      cos_sin_cache.shape[0], _stream(stream)))
+    return q_out
 
 
 def store_kvcache(key, value, k_cache, v_cache, slot_mapping, stream=None):

@@ -102,6 +102,47 @@ int pkv_qk_norm_rope(const void* q, int64_t q_row_stride, const void* k, int64_t
                     fn);
 }
 
+int pkv_qk_norm_rope_store(const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride,
+                           const void* v, int64_t v_row_stride, void* q_out, void* k_out, void* k_cache,
+                           void* v_cache, int64_t num_slots, const int32_t* slot_mapping, const int64_t* positions,
+                           int32_t n_tokens, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           const void* q_norm_weight, const void* k_norm_weight, float eps,
+                           const float* cos_sin_cache, int32_t max_position, void* stream) {
+    const char* fn = "pkv_qk_norm_rope_store";
+    int rc = check_heads(fn, num_q_heads, num_kv_heads, head_dim);
+    if (rc) return rc;
+    PKV_REQUIRE(n_tokens >= 0, PKV_ERR_INVALID_ARG, "%s: n_tokens must be >= 0 (got %d)", fn, n_tokens);
+    PKV_REQUIRE(num_slots >= 0, PKV_ERR_INVALID_ARG, "%s: num_slots must be >= 0", fn);
+    if (n_tokens == 0) return ok();
+    PKV_REQUIRE(q && k && v && q_out && k_cache && v_cache && slot_mapping && positions && q_norm_weight &&
+                    k_norm_weight && cos_sin_cache,
+                PKV_ERR_INVALID_ARG, "%s: a required pointer is NULL (only k_out may be NULL)", fn);
+    const int64_t qw = (int64_t)num_q_heads * head_dim, kw = (int64_t)num_kv_heads * head_dim;
+    PKV_REQUIRE(q_row_stride >= qw, PKV_ERR_INVALID_ARG, "%s: q_row_stride %lld < num_q_heads*head_dim %lld", fn,
+                (long long)q_row_stride, (long long)qw);
+    PKV_REQUIRE(k_row_stride >= kw && v_row_stride >= kw, PKV_ERR_INVALID_ARG,
+                "%s: k/v row strides (%lld, %lld) must be >= num_kv_heads*head_dim %lld", fn,
+                (long long)k_row_stride, (long long)v_row_stride, (long long)kw);
+    PKV_REQUIRE(q_row_stride % 8 == 0 && k_row_stride % 8 == 0 && v_row_stride % 8 == 0, PKV_ERR_INVALID_ARG,
+                "%s: row strides must be multiples of 8 elements (16-byte rows)", fn);
+    PKV_REQUIRE(((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)q_out | (uintptr_t)k_out |
+                 (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)q_norm_weight | (uintptr_t)k_norm_weight |
+                 (uintptr_t)cos_sin_cache) % 16 == 0,
+                PKV_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
+    PKV_REQUIRE(max_position > 0, PKV_ERR_INVALID_ARG, "%s: max_position must be > 0", fn);
+    PKV_REQUIRE(eps >= 0.f, PKV_ERR_INVALID_ARG, "%s: eps must be >= 0", fn);
+    PKV_REQUIRE(k_cache != v_cache, PKV_ERR_INVALID_ARG, "%s: k_cache and v_cache must be distinct", fn);
+    PKV_REQUIRE(q_out != q || q_row_stride == qw, PKV_ERR_INVALID_ARG,
+                "%s: in-place q needs q_row_stride == num_q_heads*head_dim", fn);
+    PKV_REQUIRE(!k_out || k_out != k || k_row_stride == kw, PKV_ERR_INVALID_ARG,
+                "%s: in-place k needs k_row_stride == num_kv_heads*head_dim", fn);
+    return launched(pkv::launch_qk_norm_rope_store(q, q_row_stride, k, k_row_stride, v, v_row_stride, q_out, k_out,
+                                                   k_cache, v_cache, num_slots, slot_mapping, positions, n_tokens,
+                                                   num_q_heads, num_kv_heads, q_norm_weight, k_norm_weight, eps,
+                                                   cos_sin_cache, max_position, (hipStream_t)stream),
+                    fn);
+}
+
 int pkv_store_kvcache(const void* key, int64_t key_row_stride, const void* value, int64_t value_row_stride,
                       void* k_cache, void* v_cache, int64_t num_slots, const int32_t* slot_mapping,
                       int32_t n_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t elem_bytes, void* stream) {

@@ -204,18 +204,22 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
         bool ok;
         (void)tile_row0(t, ok);
         // ---- S^T = K Q^T for two 32-key halves
+        // The two key halves are independent accumulation chains; interleaving them
+        // keeps consecutive MFMAs independent so each issues without waiting for the
+        // previous result.
         f32x16 s[2];
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
+        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kh][r] = 0.f;
-            const unsigned char* kr = kb + (32 * kh + (lane & 31)) * kKPitch + 16 * h32;
 #pragma unroll
-            for (int st = 0; st < 8; ++st) {
+        for (int st = 0; st < 8; ++st)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                const unsigned char* kr = kb + (32 * kh + (lane & 31)) * kKPitch + 16 * h32;
                 const bf16x8 av = *reinterpret_cast<const bf16x8*>(kr + 32 * st);
                 s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[st], s[kh], 0, 0, 0);
             }
-        }
         // s[kh][r] = raw score of key j0 + 32kh + 8(r/4) + 4*h32 + r%4 for query qi.
         const bool need_mask = !ok || (j0 + kKT - 1 > off + wp0) || (j0 + kKT > Lk);
         if (need_mask) {

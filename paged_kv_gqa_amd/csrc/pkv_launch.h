@@ -17,6 +17,13 @@ hipError_t launch_qk_norm_rope(const void* q, int64_t q_row_stride, const void* 
                                int32_t hq, int32_t hkv, const void* gq, const void* gk, float eps,
                                const float* table, int32_t max_pos, hipStream_t stream);
 
+hipError_t launch_qk_norm_rope_store(const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride,
+                                     const void* v, int64_t v_row_stride, void* q_out, void* k_out, void* k_cache,
+                                     void* v_cache, int64_t num_slots, const int32_t* slot_mapping,
+                                     const int64_t* positions, int32_t n_tokens, int32_t hq, int32_t hkv,
+                                     const void* gq, const void* gk, float eps, const float* table, int32_t max_pos,
+                                     hipStream_t stream);
+
 hipError_t launch_store_kvcache(const void* key, int64_t key_row_stride, const void* value,
                                 int64_t value_row_stride, void* k_cache, void* v_cache, int64_t num_slots,
                                 const int32_t* slot_mapping, int32_t n_tokens, int64_t row_bytes,

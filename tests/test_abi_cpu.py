@@ -117,3 +117,26 @@ def test_decode_validation_and_workspace(lib):
     assert f(*a) == -1
     a = list(base); a[7] = 0                          # empty batch
     assert f(*a) == 0
+
+
+def test_qk_norm_rope_store_validation(lib):
+    f = lib.pkv_qk_norm_rope_store
+    # q, qs, k, ks, v, vs, q_out, k_out, k_cache, v_cache, num_slots, slot, pos, n, Hq, Hkv, d, gq, gk, eps, tab, maxpos
+    base = [FAKE, 6144, FAKE, 6144, FAKE, 6144, FAKE, None, ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000), 4096,
+            FAKE, FAKE, 4, 32, 8, 128, FAKE, FAKE, 1e-6, FAKE, 40960, None]
+    a = list(base); a[5] = 512               # v stride shorter than the row
+    assert f(*a) == -1 and "stride" in _err(lib)
+    a = list(base); a[9] = a[8]              # k_cache == v_cache
+    assert f(*a) == -1 and "distinct" in _err(lib)
+    a = list(base); a[11] = None             # slot_mapping missing
+    assert f(*a) == -1
+    a = list(base); a[4] = ctypes.c_void_p(0x1008)   # misaligned v
+    assert f(*a) == -1 and "aligned" in _err(lib)
+    a = list(base); a[16] = 64               # head_dim
+    assert f(*a) == -2
+    a = list(base); a[10] = -1               # negative pool size
+    assert f(*a) == -1
+    a = list(base); a[7] = a[2]              # in place k with a strided k
+    assert f(*a) == -1 and "in-place" in _err(lib)
+    a = list(base); a[13] = 0                # zero tokens: nothing to do
+    assert f(*a) == 0
