@@ -234,6 +234,9 @@ def main():
     }
     log(json.dumps(kernels))
 
+    ladder = decode_graph_ladder(pkv, torch, s8, table, qkv_d, kc_d, vc_d, pos_d, slot_d, cl_d, bt_d, gq_d, gk_d,
+                                 args, log)
+
     cpu = cpu_pre = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, wd, kc_d, vc_d, qo_d, log)
@@ -270,9 +273,44 @@ def main():
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "cpu_baseline": cpu,
+        "decode_graph": ladder,
         "cpu_baseline_prefill": cpu_pre,
     }
     print(json.dumps(out), flush=True)
+
+
+def decode_graph_ladder(pkv, torch, s8, table, qkv_d, kc_d, vc_d, pos_d, slot_d, cl_d, bt_d, gq_d, gk_d, args, log):
+    """Decode step (QK-Norm + RoPE + scatter, paged decode) per batch bucket: eager vs HIP-graph replay.
+
+    Batch B runs the first B sequences of the decode workload.  "latency": host wall
+    time of one step from launch to completion (launch, then synchronise), averaged;
+    "back_to_back": wall time of consecutive steps without synchronisation, per step.
+    """
+    B = qkv_d.shape[0]
+    st = pkv.DecodeStep(qkv_d, kc_d, vc_d, pos_d, slot_d, cl_d, bt_d, gq_d, gk_d, table, s8.num_q_heads,
+                        s8.num_kv_heads, eps=s8.eps)
+    st.capture()
+    reps = max(args.steps, 20)
+    out = {"workload": "first B sequences of the decode workload, one step = qk_norm_rope_store + paged decode",
+           "unit": "us/step", "latency": {"eager": {}, "graph": {}}, "back_to_back": {"eager": {}, "graph": {}}}
+    for b in st.buckets:
+        for mode, fn in (("eager", st.run), ("graph", st.replay)):
+            for _ in range(3):
+                fn(b)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                fn(b)
+                torch.cuda.synchronize()
+            out["latency"][mode][str(b)] = round((time.perf_counter() - t0) * 1e6 / reps, 2)
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                fn(b)
+            torch.cuda.synchronize()
+            out["back_to_back"][mode][str(b)] = round((time.perf_counter() - t0) * 1e6 / reps, 2)
+    st.close()
+    log(f"decode graph ladder (us/step): {json.dumps(out)}")
+    return out
 
 
 def cpu_baseline(args, wd, kc_d, vc_d, q_d, log):

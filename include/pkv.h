@@ -9,9 +9,10 @@
  *   pkv_attn_prefill_varlen  varlen causal GQA prefill (fresh K/V or paged)
  *   pkv_attn_decode_paged    single-token paged decode
  *
- * plus pkv_rope_cache_build, which fills the cos/sin table once at set-up, and
+ * plus pkv_rope_cache_build, which fills the cos/sin table once at set-up,
  * pkv_qk_norm_rope_store, the first two steps in one pass (rotated k and v go
- * straight to their cache rows).
+ * straight to their cache rows), and the decode step (pkv_decode_step) with
+ * its HIP-graph replay per batch bucket (pkv_decode_graph_*).
  *
  * Conventions for every entry point
  *   - Every pointer argument is a DEVICE pointer owned by the caller, unless
@@ -227,6 +228,86 @@ PKV_API int pkv_attn_decode_paged(const void* q, const void* k_cache, const void
                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                           int32_t block_size, int64_t num_blocks, float softmax_scale, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * The decode step of the attention core, eager or from HIP graphs,
+ * [Walk] "Misc implementation details" (graphs for the decode stage, one per
+ * batch size 1, 2, 4, 8, ...; the smallest one that fits is replayed);
+ * [Ops] s7.1 (padded rows carry slot -1 and are not written).
+ *
+ * One step over `batch` sequences is
+ *     pkv_qk_norm_rope_store(q, k, v columns of qkv rows 0..batch-1 -> q_out,
+ *                            k_cache / v_cache at slot_mapping)
+ *     pkv_attn_decode_paged(q_out -> o, context_lens, block_table)
+ * on the buffers the descriptor names.  Those buffers are owned by the caller,
+ * sized for max_batch rows, and must stay allocated and at the same addresses
+ * while a graph built from the descriptor exists (a graph bakes them in): a
+ * caller writes each step's inputs into them, then launches.
+ */
+typedef struct {
+    const void* qkv;             /* bf16 [max_batch][qkv_row_stride]: q | k | v column blocks (a1 views) */
+    int64_t qkv_row_stride;      /* elements, >= (Hq + 2 Hkv) * head_dim, multiple of 8 */
+    void* q_out;                 /* bf16 [max_batch][Hq][head_dim], q' of the step */
+    void* o;                     /* bf16 [max_batch][Hq][head_dim], attention output */
+    void* k_cache;               /* bf16 [num_blocks][block_size][Hkv][head_dim] */
+    void* v_cache;
+    int64_t num_blocks;
+    const int64_t* positions;    /* int64 [max_batch] */
+    int32_t* slot_mapping;       /* int32 [max_batch]; a graph launch writes -1 into padded rows */
+    int32_t* context_lens;       /* int32 [max_batch]; a graph launch writes 0 into padded rows */
+    const int32_t* block_table;  /* int32 [max_batch][max_blocks_per_seq] */
+    int32_t max_blocks_per_seq;
+    int32_t max_batch;
+    const void* q_norm_weight;   /* bf16 [head_dim] */
+    const void* k_norm_weight;
+    const float* cos_sin_cache;  /* fp32 [max_position][head_dim] */
+    int32_t max_position;
+    float eps;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;            /* 128 */
+    int32_t block_size;          /* 256 */
+    float softmax_scale;
+    int32_t reserved;            /* set to 0 */
+    void* workspace;             /* >= pkv_decode_step_workspace_bytes(max_batch, ...), 256-byte aligned */
+    size_t workspace_bytes;
+} pkv_decode_step_desc;
+
+#define PKV_DECODE_GRAPH_MAX_BUCKETS 16
+
+/* Decode workspace that serves every batch size 1..max_batch (0 on invalid sizes). */
+PKV_API size_t pkv_decode_step_workspace_bytes(int32_t max_batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size);
+
+/* One eager decode step over rows 0..batch-1 (0 <= batch <= max_batch) on `stream`. */
+PKV_API int pkv_decode_step(const pkv_decode_step_desc* desc, int32_t batch, void* stream);
+
+typedef struct pkv_decode_graph_s* pkv_decode_graph;
+
+/*
+ * Captures one graph per bucket (strictly increasing, each in [1, max_batch],
+ * at most PKV_DECODE_GRAPH_MAX_BUCKETS) on a private stream of the current
+ * device; graph n is the eager step at batch n.  The descriptor is copied.
+ * Set-up only: capture and instantiation allocate host and driver objects.
+ * On failure *out is NULL and nothing is kept.
+ */
+PKV_API int pkv_decode_graph_create(const pkv_decode_step_desc* desc, const int32_t* buckets, int32_t num_buckets,
+                                    pkv_decode_graph* out);
+
+/* The bucket a batch of this size runs in (the smallest that holds it), or -1. */
+PKV_API int32_t pkv_decode_graph_bucket(pkv_decode_graph graph, int32_t batch);
+
+/*
+ * Runs a step for rows 0..batch-1: with n = pkv_decode_graph_bucket(batch),
+ * rows batch..n-1 of slot_mapping / context_lens are set to -1 / 0 by one
+ * small kernel, then graph n is launched on `stream` (same device as the
+ * capture).  Outputs of padded rows are zero.  batch == 0 does nothing;
+ * batch above the largest bucket is PKV_ERR_INVALID_ARG.  No allocation.
+ */
+PKV_API int pkv_decode_graph_launch(pkv_decode_graph graph, int32_t batch, void* stream);
+
+/* Releases the graphs (NULL is ignored).  Work already launched is unaffected. */
+PKV_API void pkv_decode_graph_destroy(pkv_decode_graph graph);
 
 #ifdef __cplusplus
 }

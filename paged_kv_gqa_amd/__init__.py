@@ -17,6 +17,9 @@ Entry points mirror the calls the attention pages describe
                             max_seqlen_q, max_seqlen_k, softmax_scale, causal, block_table)
 * ``attn_decode_paged``  -- flash_attn_with_kvcache(q, k_cache, v_cache, cache_seqlens,
                             block_table, softmax_scale, causal)
+* ``DecodeStep``         -- the decode step (QK-Norm + RoPE + scatter, then paged
+                            decode) over static buffers, eager or replayed from
+                            HIP graphs captured per batch bucket
 """
 from __future__ import annotations
 
@@ -34,7 +37,27 @@ _STATUS = {-1: "invalid argument", -2: "unsupported", -3: "launch failed", -4: "
 
 #: every symbol include/pkv.h declares
 EXPORTED = ("pkv_last_error", "pkv_version", "pkv_rope_cache_build", "pkv_qk_norm_rope",
-            "pkv_qk_norm_rope_store", "pkv_store_kvcache", "pkv_attn_prefill_varlen", "pkv_attn_decode_workspace_bytes", "pkv_attn_decode_paged")
+            "pkv_qk_norm_rope_store", "pkv_store_kvcache", "pkv_attn_prefill_varlen",
+            "pkv_attn_decode_workspace_bytes", "pkv_attn_decode_paged", "pkv_decode_step_workspace_bytes",
+            "pkv_decode_step", "pkv_decode_graph_create", "pkv_decode_graph_bucket", "pkv_decode_graph_launch",
+            "pkv_decode_graph_destroy")
+
+#: the batch ladder the decode graphs are captured for
+GRAPH_BUCKETS = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
+
+
+class DecodeStepDesc(ctypes.Structure):
+    """Mirror of pkv_decode_step_desc (include/pkv.h), field for field."""
+    _fields_ = [("qkv", ctypes.c_void_p), ("qkv_row_stride", ctypes.c_int64), ("q_out", ctypes.c_void_p),
+                ("o", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("num_blocks", ctypes.c_int64), ("positions", ctypes.c_void_p), ("slot_mapping", ctypes.c_void_p),
+                ("context_lens", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("max_blocks_per_seq", ctypes.c_int32), ("max_batch", ctypes.c_int32),
+                ("q_norm_weight", ctypes.c_void_p), ("k_norm_weight", ctypes.c_void_p),
+                ("cos_sin_cache", ctypes.c_void_p), ("max_position", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 _lib = None
 
@@ -75,6 +98,19 @@ def load_library(path: str = LIB_PATH):
     lib.pkv_attn_decode_workspace_bytes.restype = SZ
     lib.pkv_attn_decode_paged.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I64, F32, P, SZ, P]
     lib.pkv_attn_decode_paged.restype = ctypes.c_int
+    DP = ctypes.POINTER(DecodeStepDesc)
+    lib.pkv_decode_step_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
+    lib.pkv_decode_step_workspace_bytes.restype = SZ
+    lib.pkv_decode_step.argtypes = [DP, I32, P]
+    lib.pkv_decode_step.restype = ctypes.c_int
+    lib.pkv_decode_graph_create.argtypes = [DP, ctypes.POINTER(I32), I32, ctypes.POINTER(P)]
+    lib.pkv_decode_graph_create.restype = ctypes.c_int
+    lib.pkv_decode_graph_bucket.argtypes = [P, I32]
+    lib.pkv_decode_graph_bucket.restype = I32
+    lib.pkv_decode_graph_launch.argtypes = [P, I32, P]
+    lib.pkv_decode_graph_launch.restype = ctypes.c_int
+    lib.pkv_decode_graph_destroy.argtypes = [P]
+    lib.pkv_decode_graph_destroy.restype = None
     _lib = lib
     return lib
 
@@ -283,3 +319,95 @@ def attn_decode_paged(q, k_cache, v_cache, cache_seqlens, block_table, softmax_s
                                      _ptr(block_table), mb, B, hq, hkv, HEAD_DIM, BLOCK_SIZE, num_blocks,
                                      float(scale), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+class DecodeStep:
+    """The decode step over static buffers sized for ``max_batch`` rows.
+
+    ``qkv`` [max_batch, W] bf16 holds the step's q | k | v columns; ``positions``
+    (int64), ``slot_mapping`` and ``context_lens`` (int32) [max_batch] and
+    ``block_table`` [max_batch, max_blocks] are written by the caller before
+    each step.  ``run(batch)`` launches the kernels eagerly; ``capture()``
+    records one HIP graph per bucket and ``replay(batch)`` pads rows
+    [batch, bucket) (slot -1, context 0) and launches the bucket's graph.
+    Outputs: ``q_out`` (q') and ``o`` [max_batch, Hq, 128].
+    """
+
+    def __init__(self, qkv, k_cache, v_cache, positions, slot_mapping, context_lens, block_table, q_norm_weight,
+                 k_norm_weight, cos_sin_cache, num_q_heads: int, num_kv_heads: int, eps: float = 1.0e-6,
+                 softmax_scale: Optional[float] = None):
+        import torch
+        lib = load_library()
+        mb = qkv.shape[0]
+        if qkv.dtype != torch.bfloat16 or qkv.dim() != 2 or qkv.stride(1) != 1:
+            raise ValueError("qkv must be a bf16 [max_batch, W] tensor with unit column stride")
+        for t, name in ((positions, "positions"), (slot_mapping, "slot_mapping"), (context_lens, "context_lens"),
+                        (block_table, "block_table")):
+            if t.shape[0] != mb or not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous with max_batch = {mb} rows")
+        if positions.dtype != torch.int64:
+            raise TypeError("positions must be int64")
+        _i32(slot_mapping, "slot_mapping")
+        _i32(context_lens, "context_lens")
+        _i32(block_table, "block_table")
+        if k_cache.dim() != 4 or k_cache.shape[1] != BLOCK_SIZE or not (k_cache.is_contiguous() and
+                                                                        v_cache.is_contiguous()):
+            raise ValueError("caches must be contiguous [num_blocks, 256, Hkv, 128]")
+        self.q_out = torch.empty((mb, num_q_heads, HEAD_DIM), dtype=torch.bfloat16, device=qkv.device)
+        self.o = torch.empty_like(self.q_out)
+        need = int(lib.pkv_decode_step_workspace_bytes(mb, num_q_heads, num_kv_heads, HEAD_DIM, block_table.shape[1],
+                                                       BLOCK_SIZE))
+        if need == 0:
+            raise ValueError("invalid decode sizes")
+        self.workspace = torch.empty(need, dtype=torch.uint8, device=qkv.device)
+        self._keep = (qkv, k_cache, v_cache, positions, slot_mapping, context_lens, block_table, q_norm_weight,
+                      k_norm_weight, cos_sin_cache)
+        self.max_batch = mb
+        self.desc = DecodeStepDesc(
+            qkv=_ptr(qkv), qkv_row_stride=qkv.stride(0), q_out=_ptr(self.q_out), o=_ptr(self.o),
+            k_cache=_ptr(k_cache), v_cache=_ptr(v_cache), num_blocks=k_cache.shape[0], positions=_ptr(positions),
+            slot_mapping=_ptr(slot_mapping), context_lens=_ptr(context_lens), block_table=_ptr(block_table),
+            max_blocks_per_seq=block_table.shape[1], max_batch=mb, q_norm_weight=_ptr(q_norm_weight),
+            k_norm_weight=_ptr(k_norm_weight), cos_sin_cache=_ptr(cos_sin_cache),
+            max_position=cos_sin_cache.shape[0], eps=float(eps), num_q_heads=num_q_heads,
+            num_kv_heads=num_kv_heads, head_dim=HEAD_DIM, block_size=BLOCK_SIZE,
+            softmax_scale=HEAD_DIM ** -0.5 if softmax_scale is None else float(softmax_scale), reserved=0,
+            workspace=_ptr(self.workspace), workspace_bytes=need)
+        self._graph = None
+        self.buckets = ()
+
+    def run(self, batch: int, stream=None):
+        """One eager step over rows 0..batch-1."""
+        _check("pkv_decode_step", _lib.pkv_decode_step(ctypes.byref(self.desc), int(batch), _stream(stream)))
+
+    def capture(self, buckets=None):
+        """Capture one graph per bucket (default: the ladder up to max_batch)."""
+        if buckets is None:
+            buckets = [b for b in GRAPH_BUCKETS if b <= self.max_batch]
+        self.close()
+        arr = (ctypes.c_int32 * len(buckets))(*buckets)
+        h = ctypes.c_void_p()
+        _check("pkv_decode_graph_create",
+               _lib.pkv_decode_graph_create(ctypes.byref(self.desc), arr, len(buckets), ctypes.byref(h)))
+        self._graph = h
+        self.buckets = tuple(int(b) for b in buckets)
+
+    def bucket(self, batch: int) -> int:
+        return int(_lib.pkv_decode_graph_bucket(self._graph, int(batch))) if self._graph else -1
+
+    def replay(self, batch: int, stream=None):
+        """One step over rows 0..batch-1 from the captured graph of its bucket."""
+        if self._graph is None:
+            raise RuntimeError("capture() first")
+        _check("pkv_decode_graph_launch", _lib.pkv_decode_graph_launch(self._graph, int(batch), _stream(stream)))
+
+    def close(self):
+        if self._graph is not None:
+            _lib.pkv_decode_graph_destroy(self._graph)
+            self._graph = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

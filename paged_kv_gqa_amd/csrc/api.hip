@@ -50,6 +50,16 @@ int check_heads(const char* fn, int32_t hq, int32_t hkv, int32_t head_dim) {
 
 }  // namespace
 
+namespace pkv {
+int set_error(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+}  // namespace pkv
+
 extern "C" {
 
 const char* pkv_last_error(void) { return g_err; }

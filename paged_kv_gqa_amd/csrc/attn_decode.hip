@@ -327,12 +327,20 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
     }
 }
 
-// One workgroup of 128 threads per (b, h): merge the splits in order.
+// One workgroup of 128 threads per (b, h): merge the splits in order.  The
+// splits are taken 128 at a time: their (m, l) pairs are loaded by the whole
+// workgroup at once and their weights exp2(m_s - M) staged in LDS, then each
+// thread (one output dim) sums its column of partial outputs with the loads
+// unrolled, so a long context (many splits) costs a few memory latencies, not
+// one per split.  The sums run over s in increasing order, as a serial merge.
 __global__ void __launch_bounds__(128) decode_combine_kernel(const int32_t* __restrict__ context_lens,
                                                              int32_t max_blocks, int32_t hq, int32_t split_blocks,
                                                              int32_t max_splits, const float* __restrict__ part_o,
                                                              const float* __restrict__ part_ml,
                                                              uint16_t* __restrict__ o) {
+    __shared__ float s_w[128];
+    __shared__ float s_l[128];
+    __shared__ float s_red[2];
     const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
     int ctx = context_lens[b];
     const int cap = max_blocks * kBlockSize;
@@ -341,14 +349,31 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(const int32_t* __re
     const int ns = (nblk + split_blocks - 1) / split_blocks;
     const int64_t bh = (int64_t)b * hq + h;
     const float* ml = part_ml + bh * max_splits * 2;
+    const float* po = part_o + bh * max_splits * kHeadDim + d;
+
     float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
+    for (int s = d; s < ns; s += 128) M = fmaxf(M, ml[2 * s]);
+    M = wave_max(M);
+    if ((d & 63) == 0) s_red[d >> 6] = M;
+    __syncthreads();
+    M = fmaxf(s_red[0], s_red[1]);
     const float ref = M == -INFINITY ? 0.f : M;
+
     float L = 0.f, acc = 0.f;
-    for (int s = 0; s < ns; ++s) {
-        const float w = exp2f(ml[2 * s] - ref);
-        L = fmaf(ml[2 * s + 1], w, L);
-        acc = fmaf(part_o[(bh * max_splits + s) * kHeadDim + d], w, acc);
+    for (int s0 = 0; s0 < ns; s0 += 128) {
+        const int n = ns - s0 < 128 ? ns - s0 : 128;
+        if (d < n) {
+            s_w[d] = exp2f(ml[2 * (s0 + d)] - ref);
+            s_l[d] = ml[2 * (s0 + d) + 1];
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int i = 0; i < n; ++i) {
+            const float w = s_w[i];
+            L = fmaf(s_l[i], w, L);
+            acc = fmaf(po[(int64_t)(s0 + i) * kHeadDim], w, acc);
+        }
+        __syncthreads();
     }
     const float r = L > 0.f ? acc / L : 0.f;
     o[bh * kHeadDim + d] = __builtin_bit_cast(uint16_t, (bf16)r);

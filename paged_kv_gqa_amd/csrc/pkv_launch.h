@@ -9,6 +9,9 @@
 
 namespace pkv {
 
+// Sets the thread-local message pkv_last_error() returns; returns code.
+int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
 hipError_t launch_rope_cache_build(float* table, int32_t max_pos, int32_t rot_dim, double theta,
                                    hipStream_t stream);
 

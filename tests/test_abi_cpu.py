@@ -140,3 +140,53 @@ def test_qk_norm_rope_store_validation(lib):
     assert f(*a) == -1 and "in-place" in _err(lib)
     a = list(base); a[13] = 0                # zero tokens: nothing to do
     assert f(*a) == 0
+
+
+def test_decode_step_desc_layout_matches_c(tmp_path):
+    """The ctypes mirror of pkv_decode_step_desc has the C compiler's offsets and size."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    fields = [f for f, _ in pkv.DecodeStepDesc._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "pkv.h"\nint main(void) {\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(pkv_decode_step_desc, {f}));\n' for f in fields)
+                   + '  printf("%zu\\n", sizeof(pkv_decode_step_desc));\n  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    want = [getattr(pkv.DecodeStepDesc, f).offset for f in fields] + [ctypes.sizeof(pkv.DecodeStepDesc)]
+    assert got == want
+
+
+def _desc(**kw):
+    d = pkv.DecodeStepDesc(qkv=0x1000, qkv_row_stride=6144, q_out=0x2000, o=0x3000, k_cache=0x4000, v_cache=0x5000,
+                           num_blocks=64, positions=0x6000, slot_mapping=0x7000, context_lens=0x8000,
+                           block_table=0x9000, max_blocks_per_seq=8, max_batch=32, q_norm_weight=0xa000,
+                           k_norm_weight=0xb000, cos_sin_cache=0xc000, max_position=40960, eps=1e-6, num_q_heads=32,
+                           num_kv_heads=8, head_dim=128, block_size=256, softmax_scale=0.088, reserved=0,
+                           workspace=0x100000, workspace_bytes=1 << 30)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_decode_graph_validation(lib):
+    need = lib.pkv_decode_step_workspace_bytes(32, 32, 8, 128, 8, 256)
+    assert need >= max(lib.pkv_attn_decode_workspace_bytes(b, 32, 8, 128, 8, 256) for b in range(1, 33))
+    assert lib.pkv_decode_step_workspace_bytes(0, 32, 8, 128, 8, 256) == 0
+    d = _desc()
+    assert lib.pkv_decode_step(ctypes.byref(d), 33, None) == -1          # batch > max_batch
+    assert lib.pkv_decode_step(ctypes.byref(d), 0, None) == 0            # empty step
+    small = _desc(workspace_bytes=need - 1)
+    assert lib.pkv_decode_step(ctypes.byref(small), 1, None) == -4       # workspace short for some batch size
+    assert lib.pkv_decode_step(ctypes.byref(_desc(qkv_row_stride=4096)), 1, None) == -1
+    h = ctypes.c_void_p(123)
+    bad = (ctypes.c_int32 * 3)(1, 4, 4)                                   # not strictly increasing
+    assert lib.pkv_decode_graph_create(ctypes.byref(d), bad, 3, ctypes.byref(h)) == -1 and h.value is None
+    big = (ctypes.c_int32 * 2)(16, 64)                                    # beyond max_batch
+    assert lib.pkv_decode_graph_create(ctypes.byref(d), big, 2, ctypes.byref(h)) == -1
+    assert lib.pkv_decode_graph_bucket(None, 3) == -1
+    assert lib.pkv_decode_graph_launch(None, 3, None) == -1
+    lib.pkv_decode_graph_destroy(None)
