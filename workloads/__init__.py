@@ -449,3 +449,43 @@ def fill_normal_bf16_(tensor, config_id: int, seed: int, stream: int, chunk_elem
         e = min(n, s + chunk_elems)
         flat[s:e].copy_(torch.randn(e - s, generator=g, device=tensor.device, dtype=torch.float32))
     return tensor
+
+
+# ----------------------------------------------------------------------------
+# inputs of the elementwise steps around the attention core (Qwen3-8B sizes,
+# "同一个 Qwen3，两种写法", section 2 config table: hidden 4096, intermediate
+# 12288, vocab 151936)
+# ----------------------------------------------------------------------------
+
+HIDDEN_8B = 4096
+INTERMEDIATE_8B = 12288
+VOCAB = 151936
+
+
+def add_rms_inputs(seed: int, n_tokens: int, hidden: int = HIDDEN_8B):
+    """(x, residual, gamma) bf16 bits: the sublayer output x ~ N(0, 1), the residual
+    stream ~ N(0, 3^2) (it accumulates over layers), gamma = 1 + 0.05 N(0, 1)."""
+    rng = rng_for(6, seed, 0)
+    x = normal_bf16(rng, (n_tokens, hidden))
+    residual = normal_bf16(rng, (n_tokens, hidden), scale=3.0)
+    return x, residual, gamma_bf16(rng, hidden)
+
+
+def silu_inputs(seed: int, n_tokens: int, intermediate: int = INTERMEDIATE_8B):
+    """gate_up rows [T, 2I] bf16 bits ~ N(0, 2^2): gate in the front half, up in the back."""
+    return normal_bf16(rng_for(7, seed, 0), (n_tokens, 2 * intermediate), scale=2.0)
+
+
+def sampler_inputs(seed: int, num_rows: int, vocab: int = VOCAB):
+    """(logits bf16 bits [B, V], temperatures fp32 [B]).
+
+    Logits ~ N(0, 2^2) with 16 favoured tokens per row raised by U(4, 12), so each
+    row has a few likely tokens and a long tail.  Temperatures U(0.3, 1.5), and
+    every 8th row 0.05 (close to greedy)."""
+    rng = rng_for(8, seed, 0)
+    lg = rng.standard_normal(size=(num_rows, vocab), dtype=np.float32) * np.float32(2.0)
+    fav = np.stack([rng.choice(vocab, size=16, replace=False) for _ in range(num_rows)])
+    lg[np.arange(num_rows)[:, None], fav] += rng.uniform(4.0, 12.0, size=fav.shape).astype(np.float32)
+    temps = rng.uniform(0.3, 1.5, size=num_rows).astype(np.float32)
+    temps[::8] = np.float32(0.05)
+    return bf16_bits(lg), temps
