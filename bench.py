@@ -234,6 +234,8 @@ def main():
     }
     log(json.dumps(kernels))
 
+    ops = sublayer_ops(pkv, torch, dev, to_dev, args, log)
+
     ladder = decode_graph_ladder(pkv, torch, s8, table, qkv_d, kc_d, vc_d, pos_d, slot_d, cl_d, bt_d, gq_d, gk_d,
                                  args, log)
 
@@ -273,10 +275,56 @@ def main():
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "cpu_baseline": cpu,
+        "sublayer_ops": ops,
         "decode_graph": ladder,
         "cpu_baseline_prefill": cpu_pre,
     }
     print(json.dumps(out), flush=True)
+
+
+def sublayer_ops(pkv, torch, dev, to_dev, args, log):
+    """The elementwise steps around attention at Qwen3-8B sizes, each timed alone with
+    events over args.steps launches: residual add + RMSNorm on the prefill's 32768
+    tokens (hidden 4096), SiluAndMul on 32768 tokens (intermediate 12288), and the
+    sampler on the decode batch's 256 rows of 151936 bf16 logits (Philox noise)."""
+    import workloads as wl
+    T, H, I, B, V = 32768, wl.HIDDEN_8B, wl.INTERMEDIATE_8B, 256, wl.VOCAB
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 31)
+    x = torch.randn((T, H), generator=gen, device=dev).to(torch.bfloat16)
+    r = (3 * torch.randn((T, H), generator=gen, device=dev)).to(torch.bfloat16)
+    g = (1 + 0.05 * torch.randn((H,), generator=gen, device=dev)).to(torch.bfloat16)
+    y, r_out = torch.empty_like(x), torch.empty_like(x)
+    gu = (2 * torch.randn((T, 2 * I), generator=gen, device=dev)).to(torch.bfloat16)
+    act = torch.empty((T, I), dtype=torch.bfloat16, device=dev)
+    lg_np, temps_np = wl.sampler_inputs(args.seed, B)
+    lg, temps = to_dev(lg_np), to_dev(temps_np)
+    tok = torch.empty(B, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+    cases = {
+        "add_rms_norm": (lambda: pkv.add_rms_norm(x, r, g, 1e-6, y=y, residual_out=r_out), T * H * 2 * 4 + H * 2,
+                         f"[{T}, {H}] bf16: read x, residual; write y, residual (32 KiB per token)"),
+        "silu_and_mul": (lambda: pkv.silu_and_mul(gu, out=act), T * I * 2 * 3,
+                         f"[{T}, 2 x {I}] bf16 -> [{T}, {I}]"),
+        "sample_gumbel": (lambda: pkv.sample_gumbel(lg, temps, seed=1, offset=0, out=tok), B * V * 2 + B * 12,
+                          f"[{B}, {V}] bf16 logits, in-kernel Philox4x32-10 noise"),
+    }
+    out = {}
+    for name, (fn, nbytes, what) in cases.items():
+        for _ in range(args.warmup):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / args.steps
+        out[name] = {"ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 2), "bytes": nbytes,
+                     "shape": what}
+    log(f"sublayer ops: {json.dumps(out)}")
+    del x, r, y, r_out, gu, act
+    return out
 
 
 def decode_graph_ladder(pkv, torch, s8, table, qkv_d, kc_d, vc_d, pos_d, slot_d, cl_d, bt_d, gq_d, gk_d, args, log):

@@ -11,8 +11,10 @@
  *
  * plus pkv_rope_cache_build, which fills the cos/sin table once at set-up,
  * pkv_qk_norm_rope_store, the first two steps in one pass (rotated k and v go
- * straight to their cache rows), and the decode step (pkv_decode_step) with
- * its HIP-graph replay per batch bucket (pkv_decode_graph_*).
+ * straight to their cache rows), the decode step (pkv_decode_step) with
+ * its HIP-graph replay per batch bucket (pkv_decode_graph_*), and the
+ * elementwise steps on either side of attention in a decoder layer:
+ * pkv_add_rms_norm, pkv_silu_and_mul and the sampler pkv_sample_gumbel.
  *
  * Conventions for every entry point
  *   - Every pointer argument is a DEVICE pointer owned by the caller, unless
@@ -228,6 +230,63 @@ PKV_API int pkv_attn_decode_paged(const void* q, const void* k_cache, const void
                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                           int32_t block_size, int64_t num_blocks, float softmax_scale, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_add_rms_norm -- residual add folded into RMSNorm, [Ops] s2 (RMSNorm
+ * and its residual entry point); [TwoWays] s3.6 (one pass: read x and the
+ * residual, write y and the new residual).  Per row of `hidden` elements:
+ *     s_i      = fp32(x_i) + fp32(residual_i)        (one IEEE fp32 add)
+ *     res'_i   = bf16(s_i)                           (the new residual)
+ *     r        = 1 / sqrt(mean_i s_i^2 + eps)        (fp32)
+ *     y_i      = bf16(bf16(s_i * r) * gamma_i)       (rounded, then times gamma)
+ * With residual == NULL (and residual_out == NULL) the input itself is
+ * normalised: s_i = x_i (the pages' rms_forward, used before the first layer).
+ *
+ *   x, residual, y, residual_out   bf16 contiguous [n_tokens][hidden]; y may
+ *                                  alias x and residual_out may alias residual
+ *                                  (in place); y != residual_out.
+ *   weight                         bf16 [hidden] (gamma).
+ *   hidden                         multiple of 8, at most 16384.
+ */
+PKV_API int pkv_add_rms_norm(const void* x, const void* residual, const void* weight, void* y, void* residual_out,
+                             int32_t n_tokens, int32_t hidden, float eps, void* stream);
+
+/*
+ * pkv_silu_and_mul -- SwiGLU activation, [Ops] s4.  Row t of x holds gate
+ * (columns 0..I-1) then up (columns I..2I-1):
+ *     out[t][i] = bf16(silu(gate_i) * up_i),  silu(g) = g / (1 + exp(-g)),
+ * in fp32 with one rounding.
+ *   x, x_row_stride       bf16 rows of >= 2 * intermediate elements.
+ *   out, out_row_stride   bf16 rows of >= intermediate elements; must not
+ *                         overlap x.  Strides multiples of 8 elements.
+ */
+PKV_API int pkv_silu_and_mul(const void* x, int64_t x_row_stride, void* out, int64_t out_row_stride,
+                             int32_t n_tokens, int32_t intermediate, void* stream);
+
+#define PKV_DTYPE_BF16 0
+#define PKV_DTYPE_F32 1
+
+/*
+ * pkv_sample_gumbel -- one token per row by the Gumbel-max form of sampling,
+ * [Ops] s9: logits / temperature, softmax p, E ~ Exp(1) clamped below at
+ * 1e-10, token = argmax_i p_i / E_i (lowest index on ties).  The kernel takes
+ * the argmax of the equivalent score (l_i / T) log2(e) - log2(E_i) (the
+ * softmax normaliser is the same for every token of a row), in fp32.
+ *
+ *   logits, logits_row_stride, logits_dtype   [num_rows][vocab] bf16 or fp32
+ *                      (PKV_DTYPE_*), rows 16-byte aligned.
+ *   temperatures       fp32 [num_rows], each > 0 (values below 1e-10 act as 1e-10).
+ *   noise              NULL: E is drawn in the kernel from Philox4x32-10 with
+ *                      key (seed low 32 bits, seed high 32 bits) and counter
+ *                      (column / 4, row, offset low, offset high), word column % 4;
+ *                      the top 24 bits k give u = (k + 1) / 2^24 and E = -ln(u).
+ *                      Otherwise fp32 [num_rows][noise_row_stride] holding E.
+ *   tokens             int64 [num_rows], written.
+ * Rows whose scores are all NaN return token 0.
+ */
+PKV_API int pkv_sample_gumbel(const void* logits, int64_t logits_row_stride, int32_t logits_dtype,
+                              const float* temperatures, const float* noise, int64_t noise_row_stride, uint64_t seed,
+                              uint64_t offset, int64_t* tokens, int32_t num_rows, int32_t vocab, void* stream);
 
 /*
  * The decode step of the attention core, eager or from HIP graphs,

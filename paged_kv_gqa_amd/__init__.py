@@ -17,6 +17,9 @@ Entry points mirror the calls the attention pages describe
                             max_seqlen_q, max_seqlen_k, softmax_scale, causal, block_table)
 * ``attn_decode_paged``  -- flash_attn_with_kvcache(q, k_cache, v_cache, cache_seqlens,
                             block_table, softmax_scale, causal)
+* ``add_rms_norm``       -- RMSNorm with the residual add folded in (add_rms_forward)
+* ``silu_and_mul``       -- SiluAndMul
+* ``sample_gumbel``      -- the sampler: argmax softmax(logits / T) / Exp(1) noise
 * ``DecodeStep``         -- the decode step (QK-Norm + RoPE + scatter, then paged
                             decode) over static buffers, eager or replayed from
                             HIP graphs captured per batch bucket
@@ -40,7 +43,7 @@ EXPORTED = ("pkv_last_error", "pkv_version", "pkv_rope_cache_build", "pkv_qk_nor
             "pkv_qk_norm_rope_store", "pkv_store_kvcache", "pkv_attn_prefill_varlen",
             "pkv_attn_decode_workspace_bytes", "pkv_attn_decode_paged", "pkv_decode_step_workspace_bytes",
             "pkv_decode_step", "pkv_decode_graph_create", "pkv_decode_graph_bucket", "pkv_decode_graph_launch",
-            "pkv_decode_graph_destroy")
+            "pkv_decode_graph_destroy", "pkv_add_rms_norm", "pkv_silu_and_mul", "pkv_sample_gumbel")
 
 #: the batch ladder the decode graphs are captured for
 GRAPH_BUCKETS = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
@@ -98,6 +101,12 @@ def load_library(path: str = LIB_PATH):
     lib.pkv_attn_decode_workspace_bytes.restype = SZ
     lib.pkv_attn_decode_paged.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I64, F32, P, SZ, P]
     lib.pkv_attn_decode_paged.restype = ctypes.c_int
+    lib.pkv_add_rms_norm.argtypes = [P, P, P, P, P, I32, I32, F32, P]
+    lib.pkv_add_rms_norm.restype = ctypes.c_int
+    lib.pkv_silu_and_mul.argtypes = [P, I64, P, I64, I32, I32, P]
+    lib.pkv_silu_and_mul.restype = ctypes.c_int
+    lib.pkv_sample_gumbel.argtypes = [P, I64, I32, P, P, I64, ctypes.c_uint64, ctypes.c_uint64, P, I32, I32, P]
+    lib.pkv_sample_gumbel.restype = ctypes.c_int
     DP = ctypes.POINTER(DecodeStepDesc)
     lib.pkv_decode_step_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
     lib.pkv_decode_step_workspace_bytes.restype = SZ
@@ -318,6 +327,69 @@ def attn_decode_paged(q, k_cache, v_cache, cache_seqlens, block_table, softmax_s
            lib.pkv_attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(cache_seqlens),
                                      _ptr(block_table), mb, B, hq, hkv, HEAD_DIM, BLOCK_SIZE, num_blocks,
                                      float(scale), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def add_rms_norm(x, residual, weight, eps: float = 1.0e-6, y=None, residual_out=None, stream=None):
+    """RMSNorm of x + residual over the last dim (bf16 [T, hidden], contiguous).
+
+    Returns (y, new_residual).  With residual None, plain RMSNorm of x: returns (y, x).
+    Pass y=x / residual_out=residual to run in place."""
+    import torch
+    lib = load_library()
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 [T, hidden] tensor")
+    t, hidden = x.shape
+    if residual is not None and (residual.shape != x.shape or residual.dtype != x.dtype or
+                                 not residual.is_contiguous()):
+        raise ValueError("residual must match x")
+    if y is None:
+        y = torch.empty_like(x)
+    if residual is not None and residual_out is None:
+        residual_out = torch.empty_like(x)
+    _check("pkv_add_rms_norm",
+           lib.pkv_add_rms_norm(_ptr(x), _ptr(residual), _ptr(weight), _ptr(y),
+                                _ptr(residual_out) if residual is not None else None, t, hidden, float(eps),
+                                _stream(stream)))
+    return y, (residual_out if residual is not None else x)
+
+
+def silu_and_mul(x, out=None, stream=None):
+    """x bf16 [T, 2I] (gate | up) -> silu(gate) * up, bf16 [T, I]."""
+    import torch
+    lib = load_library()
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a bf16 [T, 2I] tensor with unit column stride")
+    t, two_i = x.shape
+    inter = two_i // 2
+    if out is None:
+        out = torch.empty((t, inter), dtype=torch.bfloat16, device=x.device)
+    _check("pkv_silu_and_mul",
+           lib.pkv_silu_and_mul(_ptr(x), x.stride(0), _ptr(out), out.stride(0), t, inter, _stream(stream)))
+    return out
+
+
+def sample_gumbel(logits, temperatures, seed: int = 0, offset: int = 0, noise=None, out=None, stream=None):
+    """One token per row: argmax softmax(logits / T) / E, E ~ Exp(1) (in-kernel Philox unless
+    ``noise`` [B, V] fp32 is given).  logits bf16 or fp32 [B, V]; returns int64 [B]."""
+    import torch
+    lib = load_library()
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be [B, V] with unit column stride")
+    dt = {torch.bfloat16: 0, torch.float32: 1}.get(logits.dtype)
+    if dt is None:
+        raise TypeError("logits must be bfloat16 or float32")
+    b, v = logits.shape
+    if temperatures.dtype != torch.float32 or temperatures.numel() != b or not temperatures.is_contiguous():
+        raise ValueError("temperatures must be contiguous float32 [B]")
+    if noise is not None and (noise.dtype != torch.float32 or noise.shape != logits.shape or noise.stride(1) != 1):
+        raise ValueError("noise must be float32 [B, V]")
+    if out is None:
+        out = torch.empty(b, dtype=torch.int64, device=logits.device)
+    _check("pkv_sample_gumbel",
+           lib.pkv_sample_gumbel(_ptr(logits), logits.stride(0), dt, _ptr(temperatures), _ptr(noise),
+                                 noise.stride(0) if noise is not None else 0, int(seed), int(offset), _ptr(out), b, v,
+                                 _stream(stream)))
     return out
 
 

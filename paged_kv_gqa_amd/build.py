@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpkv.so")
 OBJDIR = os.path.join(ROOT, "_build", "pkv")
 
-SOURCES = ["api.hip", "rope.hip", "store_kvcache.hip", "attn_decode.hip", "attn_prefill.hip", "decode_graph.hip"]
+SOURCES = ["api.hip", "rope.hip", "store_kvcache.hip", "attn_decode.hip", "attn_prefill.hip", "decode_graph.hip", "sublayer.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -294,4 +294,71 @@ int pkv_attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
     return launched(pkv::launch_attn_decode(a, (hipStream_t)stream), fn);
 }
 
+int pkv_add_rms_norm(const void* x, const void* residual, const void* weight, void* y, void* residual_out,
+                     int32_t n_tokens, int32_t hidden, float eps, void* stream) {
+    const char* fn = "pkv_add_rms_norm";
+    PKV_REQUIRE(n_tokens >= 0, PKV_ERR_INVALID_ARG, "%s: n_tokens must be >= 0 (got %d)", fn, n_tokens);
+    PKV_REQUIRE(hidden > 0 && hidden % 8 == 0, PKV_ERR_INVALID_ARG, "%s: hidden %d must be a positive multiple of 8",
+                fn, hidden);
+    PKV_REQUIRE(hidden <= 8 * 256 * 8, PKV_ERR_UNSUPPORTED, "%s: hidden %d above the built maximum 16384", fn, hidden);
+    PKV_REQUIRE(eps >= 0.f, PKV_ERR_INVALID_ARG, "%s: eps must be >= 0", fn);
+    if (n_tokens == 0) return ok();
+    PKV_REQUIRE(x && weight && y, PKV_ERR_INVALID_ARG, "%s: x, weight and y are required", fn);
+    PKV_REQUIRE((residual == nullptr) == (residual_out == nullptr), PKV_ERR_INVALID_ARG,
+                "%s: residual and residual_out are given together or not at all", fn);
+    PKV_REQUIRE(!residual_out || residual_out != y, PKV_ERR_INVALID_ARG, "%s: y and residual_out must differ", fn);
+    PKV_REQUIRE(((uintptr_t)x | (uintptr_t)residual | (uintptr_t)weight | (uintptr_t)y | (uintptr_t)residual_out) %
+                        16 == 0,
+                PKV_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
+    return launched(pkv::launch_add_rms_norm(x, residual, weight, y, residual_out, n_tokens, hidden, eps,
+                                             (hipStream_t)stream),
+                    fn);
+}
+
+int pkv_silu_and_mul(const void* x, int64_t x_row_stride, void* out, int64_t out_row_stride, int32_t n_tokens,
+                     int32_t intermediate, void* stream) {
+    const char* fn = "pkv_silu_and_mul";
+    PKV_REQUIRE(n_tokens >= 0, PKV_ERR_INVALID_ARG, "%s: n_tokens must be >= 0 (got %d)", fn, n_tokens);
+    PKV_REQUIRE(intermediate > 0 && intermediate % 8 == 0, PKV_ERR_INVALID_ARG,
+                "%s: intermediate %d must be a positive multiple of 8", fn, intermediate);
+    PKV_REQUIRE(x_row_stride >= 2 * (int64_t)intermediate && out_row_stride >= intermediate, PKV_ERR_INVALID_ARG,
+                "%s: row strides (%lld, %lld) shorter than the rows", fn, (long long)x_row_stride,
+                (long long)out_row_stride);
+    PKV_REQUIRE(x_row_stride % 8 == 0 && out_row_stride % 8 == 0, PKV_ERR_INVALID_ARG,
+                "%s: row strides must be multiples of 8 elements", fn);
+    if (n_tokens == 0) return ok();
+    PKV_REQUIRE(x && out, PKV_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    PKV_REQUIRE(((uintptr_t)x | (uintptr_t)out) % 16 == 0, PKV_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned",
+                fn);
+    return launched(pkv::launch_silu_and_mul(x, x_row_stride, out, out_row_stride, n_tokens, intermediate,
+                                             (hipStream_t)stream),
+                    fn);
+}
+
+int pkv_sample_gumbel(const void* logits, int64_t logits_row_stride, int32_t logits_dtype, const float* temperatures,
+                      const float* noise, int64_t noise_row_stride, uint64_t seed, uint64_t offset, int64_t* tokens,
+                      int32_t num_rows, int32_t vocab, void* stream) {
+    const char* fn = "pkv_sample_gumbel";
+    PKV_REQUIRE(logits_dtype == PKV_DTYPE_BF16 || logits_dtype == PKV_DTYPE_F32, PKV_ERR_UNSUPPORTED,
+                "%s: logits_dtype %d unsupported (bf16 or fp32)", fn, logits_dtype);
+    PKV_REQUIRE(num_rows >= 0 && vocab > 0, PKV_ERR_INVALID_ARG, "%s: num_rows must be >= 0 and vocab > 0", fn);
+    PKV_REQUIRE(logits_row_stride >= vocab, PKV_ERR_INVALID_ARG, "%s: logits_row_stride %lld < vocab %d", fn,
+                (long long)logits_row_stride, vocab);
+    const int64_t align_elems = logits_dtype == PKV_DTYPE_BF16 ? 8 : 4;
+    PKV_REQUIRE(logits_row_stride % align_elems == 0, PKV_ERR_INVALID_ARG,
+                "%s: logits_row_stride must be a multiple of %lld elements (16-byte rows)", fn,
+                (long long)align_elems);
+    if (noise)
+        PKV_REQUIRE(noise_row_stride >= vocab && noise_row_stride % 4 == 0, PKV_ERR_INVALID_ARG,
+                    "%s: noise_row_stride must be >= vocab and a multiple of 4", fn);
+    if (num_rows == 0) return ok();
+    PKV_REQUIRE(logits && temperatures && tokens, PKV_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    PKV_REQUIRE(((uintptr_t)logits | (uintptr_t)noise) % 16 == 0, PKV_ERR_INVALID_ARG,
+                "%s: logits and noise must be 16-byte aligned", fn);
+    return launched(pkv::launch_sample_gumbel(logits, logits_row_stride, logits_dtype == PKV_DTYPE_F32, temperatures,
+                                              noise, noise_row_stride, seed, offset, tokens, num_rows, vocab,
+                                              (hipStream_t)stream),
+                    fn);
+}
+
 }  // extern "C"

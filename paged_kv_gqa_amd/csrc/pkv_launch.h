@@ -32,6 +32,17 @@ hipError_t launch_store_kvcache(const void* key, int64_t key_row_stride, const v
                                 const int32_t* slot_mapping, int32_t n_tokens, int64_t row_bytes,
                                 int32_t elem_bytes, hipStream_t stream);
 
+hipError_t launch_add_rms_norm(const void* x, const void* residual, const void* gamma, void* y, void* residual_out,
+                               int32_t n_tokens, int32_t hidden, float eps, hipStream_t stream);
+
+hipError_t launch_silu_and_mul(const void* x, int64_t x_row_stride, void* out, int64_t out_row_stride,
+                               int32_t n_tokens, int32_t inter, hipStream_t stream);
+
+hipError_t launch_sample_gumbel(const void* logits, int64_t row_stride, int32_t logits_f32,
+                                const float* temperatures, const float* noise, int64_t noise_row_stride,
+                                uint64_t seed, uint64_t offset, int64_t* tokens, int32_t num_rows, int32_t vocab,
+                                hipStream_t stream);
+
 struct PrefillArgs {
     const void* q;
     int64_t q_row_stride;

@@ -1,0 +1,336 @@
+// sublayer.hip -- the elementwise steps around the attention core (gfx950):
+// residual add + RMSNorm, SiluAndMul, and the Gumbel-max sampler.
+//
+// "3.3 Model skeleton and core operators", section 2 (RMSNorm with the
+// residual folded in: fp32 add, the sum rounded to bf16 is the new residual,
+// the fp32 sum is normalised, rounded to bf16, then multiplied by gamma in
+// bf16), section 4 (SiluAndMul: front half gate, back half up) and section 9
+// (sampler: logits / temperature, softmax, divide by Exp(1) noise clamped at
+// 1e-10, argmax).  "同一个 Qwen3，两种写法", section 3.6: the fused add + norm
+// moves 32 KiB per 4096-wide bf16 token (read x, residual; write y, residual).
+//
+// All three are HBM-streaming kernels: 16-byte vector loads and stores, fp32
+// math in registers, one pass over memory.
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// residual add + RMSNorm
+// ---------------------------------------------------------------------------
+// A row of `hidden` elements is covered by `lpr` lanes (64, 128 or 256; 256 /
+// lpr rows per 256-thread block), each owning up to NC chunks of 8 elements
+// strided by lpr chunks.  The row's sum of squares: a wave butterfly, then the
+// row's waves combine through LDS in wave order (deterministic).
+template <int NC>
+__global__ void __launch_bounds__(256) add_rms_norm_kernel(const uint16_t* x, const uint16_t* residual,
+                                                           const uint16_t* __restrict__ gamma, uint16_t* y,
+                                                           uint16_t* residual_out, int32_t n_tokens, int32_t hidden,
+                                                           int32_t lpr, float eps) {
+    __shared__ float s_part[4];
+    const int tid = threadIdx.x;
+    const int rpb = 256 / lpr;
+    const int lr = tid / lpr, li = tid - lr * lpr;
+    const int64_t row = (int64_t)blockIdx.x * rpb + lr;
+    const bool live = row < n_tokens;
+    const int chunks = hidden >> 3;
+    const int64_t base = row * hidden;
+
+    float s[NC][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+        const int c = li + k * lpr;
+        const bool ok = live && c < chunks;
+        const u32x4 xv = ok ? ldg128(x + base + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+        if (residual) {
+            const u32x4 rv = ok ? ldg128(residual + base + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                // fp32 add of the two bf16 values (exact inputs, one IEEE rounding)
+                s[k][2 * w] = bf16lo(xv[w]) + bf16lo(rv[w]);
+                s[k][2 * w + 1] = bf16hi(xv[w]) + bf16hi(rv[w]);
+            }
+        } else {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                s[k][2 * w] = bf16lo(xv[w]);
+                s[k][2 * w + 1] = bf16hi(xv[w]);
+            }
+        }
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = fmaf(s[k][e], s[k][e], part);
+        ss += part;
+        if (ok && residual_out) {
+            u32x4 ro;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) ro[w] = pack_bf16x2(s[k][2 * w], s[k][2 * w + 1]);
+            stg128(residual_out + base + 8 * c, ro);
+        }
+    }
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) s_part[tid >> 6] = ss;
+    __syncthreads();
+    const int wpr = lpr >> 6;
+    float tot = 0.f;
+    for (int j = 0; j < wpr; ++j) tot += s_part[lr * wpr + j];
+    const float r = 1.0f / sqrtf(tot / (float)hidden + eps);
+    if (!live) return;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+        const int c = li + k * lpr;
+        if (c >= chunks) break;
+        const u32x4 gv = ldg128(gamma + 8 * c);
+        u32x4 out;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            // normalised value rounded to bf16, then the bf16 product with gamma
+            const float n0 = bf16lo(pack_bf16x2(s[k][2 * w] * r, 0.f));
+            const float n1 = bf16lo(pack_bf16x2(s[k][2 * w + 1] * r, 0.f));
+            out[w] = pack_bf16x2(n0 * bf16lo(gv[w]), n1 * bf16hi(gv[w]));
+        }
+        stg128(y + base + 8 * c, out);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// SiluAndMul
+// ---------------------------------------------------------------------------
+// One lane per 8 output elements: the gate chunk and the up chunk of the same
+// columns, silu(g) * u in fp32, one rounding.
+__global__ void __launch_bounds__(256) silu_and_mul_kernel(const uint16_t* __restrict__ x, int64_t x_row_stride,
+                                                           uint16_t* __restrict__ out, int64_t out_row_stride,
+                                                           int32_t n_tokens, int32_t inter) {
+    const int cpr = inter >> 3;
+    const int64_t total = (int64_t)n_tokens * cpr;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = e / cpr;
+        const int c = (int)(e - t * cpr);
+        const uint16_t* row = x + t * x_row_stride;
+        const u32x4 gv = ldg128(row + 8 * c);
+        const u32x4 uv = ldg128(row + inter + 8 * c);
+        u32x4 o;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float g0 = bf16lo(gv[w]), g1 = bf16hi(gv[w]);
+            const float a0 = g0 / (1.0f + __expf(-g0)) * bf16lo(uv[w]);
+            const float a1 = g1 / (1.0f + __expf(-g1)) * bf16hi(uv[w]);
+            o[w] = pack_bf16x2(a0, a1);
+        }
+        stg128(out + t * out_row_stride + 8 * c, o);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Gumbel-max sampler
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon et al., SC 2011): 10 rounds of two 32x32->64-bit
+// products mixed with the counter and key; the key advances by the Weyl
+// constants between rounds.
+struct Philox4 {
+    uint32_t v[4];
+};
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                                 uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n1 = (uint32_t)p1;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n3 = (uint32_t)p0;
+        c0 = n0;
+        c1 = n1;
+        c2 = n2;
+        c3 = n3;
+    }
+    return Philox4{{c0, c1, c2, c3}};
+}
+
+// Exp(1) noise by inversion of the uniform (k + 1) / 2^24 on (0, 1] made from
+// the top 24 bits of a draw; returns log2 of the noise clamped at 1e-10.
+__device__ __forceinline__ float log2_noise_from_bits(uint32_t bits) {
+    const float u = (float)((bits >> 8) + 1u) * 0x1p-24f;
+    const float E = fmaxf(-__builtin_amdgcn_logf(u) * 0.69314718055994531f, 1e-10f);
+    return __builtin_amdgcn_logf(E);
+}
+
+// Score of a token in log2 units: log2(p_i / E_i) up to a per-row constant,
+//   = (l_i / T) * log2(e) - log2(E_i).
+// The row's softmax normaliser is common to every token, so the argmax needs
+// neither the max nor the sum.  Ties keep the lower index.
+struct Best {
+    float s;
+    int32_t i;
+};
+
+__device__ __forceinline__ void take(Best& b, float s, int32_t i) {
+    if (s > b.s || (s == b.s && i < b.i)) {
+        b.s = s;
+        b.i = i;
+    }
+}
+
+template <bool F32>
+__device__ __forceinline__ void load8(const void* row, int64_t c8, float (&l)[8]) {
+    if (F32) {
+        const float* p = (const float*)row + 8 * c8;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            l[e] = a[e];
+            l[4 + e] = b[e];
+        }
+    } else {
+        const u32x4 v = ldg128((const uint16_t*)row + 8 * c8);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            l[2 * w] = bf16lo(v[w]);
+            l[2 * w + 1] = bf16hi(v[w]);
+        }
+    }
+}
+
+constexpr int kSampThreads = 512;
+
+template <bool F32>
+__global__ void __launch_bounds__(kSampThreads) sample_gumbel_kernel(
+    const void* __restrict__ logits, int64_t row_stride, const float* __restrict__ temperatures,
+    const float* __restrict__ noise, int64_t noise_row_stride, uint32_t k0, uint32_t k1, uint32_t off_lo,
+    uint32_t off_hi, int64_t* __restrict__ tokens, int32_t vocab) {
+    __shared__ float s_s[kSampThreads / 64];
+    __shared__ int32_t s_i[kSampThreads / 64];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const float T = fmaxf(temperatures[b], 1e-10f);
+    const float mul = 1.4426950408889634f / T;  // log2(e) / T
+    const char* row = (const char*)logits + (int64_t)b * row_stride * (F32 ? 4 : 2);
+    const float* nrow = noise ? noise + (int64_t)b * noise_row_stride : nullptr;
+    Best best{-INFINITY, 0x7FFFFFFF};
+    const int64_t n8 = vocab >> 3;
+    for (int64_t c = tid; c < n8; c += kSampThreads) {
+        float l[8];
+        load8<F32>(row, c, l);
+        float ln[8];
+        if (nrow) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(nrow + 8 * c);
+            const f32x4 bq = *reinterpret_cast<const f32x4*>(nrow + 8 * c + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ln[e] = __builtin_amdgcn_logf(fmaxf(a[e], 1e-10f));
+                ln[4 + e] = __builtin_amdgcn_logf(fmaxf(bq[e], 1e-10f));
+            }
+        } else {
+            const uint32_t q = (uint32_t)(2 * c);  // Philox counter word 0: column / 4
+            const Philox4 r0 = philox4x32_10(q, (uint32_t)b, off_lo, off_hi, k0, k1);
+            const Philox4 r1 = philox4x32_10(q + 1, (uint32_t)b, off_lo, off_hi, k0, k1);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ln[e] = log2_noise_from_bits(r0.v[e]);
+                ln[4 + e] = log2_noise_from_bits(r1.v[e]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) take(best, l[e] * mul - ln[e], (int32_t)(8 * c + e));
+    }
+    // tail of a vocab that is not a multiple of 8
+    for (int32_t i = (int32_t)(n8 << 3) + tid; i < vocab; i += kSampThreads) {
+        const float l = F32 ? ((const float*)row)[i] : bf16lo(((const uint16_t*)row)[i]);
+        float ln;
+        if (nrow) {
+            ln = __builtin_amdgcn_logf(fmaxf(nrow[i], 1e-10f));
+        } else {
+            const Philox4 r = philox4x32_10((uint32_t)(i >> 2), (uint32_t)b, off_lo, off_hi, k0, k1);
+            ln = log2_noise_from_bits(r.v[i & 3]);
+        }
+        take(best, l * mul - ln, i);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float s = __shfl_xor(best.s, o, 64);
+        const int32_t i = __shfl_xor(best.i, o, 64);
+        take(best, s, i);
+    }
+    if ((tid & 63) == 0) {
+        s_s[tid >> 6] = best.s;
+        s_i[tid >> 6] = best.i;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        Best r{s_s[0], s_i[0]};
+        for (int w = 1; w < kSampThreads / 64; ++w) take(r, s_s[w], s_i[w]);
+        // every score NaN (NaN logits): fall back to token 0
+        tokens[b] = r.i == 0x7FFFFFFF ? 0 : r.i;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_add_rms_norm(const void* x, const void* residual, const void* gamma, void* y, void* residual_out,
+                               int32_t n_tokens, int32_t hidden, float eps, hipStream_t stream) {
+    if (n_tokens == 0) return hipSuccess;
+    const int chunks = hidden / 8;
+    const int lpr = chunks <= 64 ? 64 : (chunks <= 128 ? 128 : 256);
+    const int nc = (chunks + lpr - 1) / lpr;
+    const int rpb = 256 / lpr;
+    const unsigned blocks = (unsigned)(((int64_t)n_tokens + rpb - 1) / rpb);
+#define PKV_RMS_CASE(N)                                                                                            \
+    case N:                                                                                                        \
+        hipLaunchKernelGGL(add_rms_norm_kernel<N>, dim3(blocks), dim3(256), 0, stream, (const uint16_t*)x,        \
+                           (const uint16_t*)residual, (const uint16_t*)gamma, (uint16_t*)y, (uint16_t*)residual_out, \
+                           n_tokens, hidden, lpr, eps);                                                            \
+        break;
+    switch (nc) {
+        PKV_RMS_CASE(1)
+        PKV_RMS_CASE(2)
+        PKV_RMS_CASE(3)
+        PKV_RMS_CASE(4)
+        PKV_RMS_CASE(5)
+        PKV_RMS_CASE(6)
+        PKV_RMS_CASE(7)
+        PKV_RMS_CASE(8)
+        default:
+            return hipErrorInvalidValue;
+    }
+#undef PKV_RMS_CASE
+    return hipGetLastError();
+}
+
+hipError_t launch_silu_and_mul(const void* x, int64_t x_row_stride, void* out, int64_t out_row_stride,
+                               int32_t n_tokens, int32_t inter, hipStream_t stream) {
+    const int64_t total = (int64_t)n_tokens * (inter / 8);
+    if (total == 0) return hipSuccess;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(silu_and_mul_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const uint16_t*)x,
+                       x_row_stride, (uint16_t*)out, out_row_stride, n_tokens, inter);
+    return hipGetLastError();
+}
+
+hipError_t launch_sample_gumbel(const void* logits, int64_t row_stride, int32_t logits_f32,
+                                const float* temperatures, const float* noise, int64_t noise_row_stride,
+                                uint64_t seed, uint64_t offset, int64_t* tokens, int32_t num_rows, int32_t vocab,
+                                hipStream_t stream) {
+    if (num_rows == 0) return hipSuccess;
+    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    const uint32_t o0 = (uint32_t)offset, o1 = (uint32_t)(offset >> 32);
+    if (logits_f32)
+        hipLaunchKernelGGL(sample_gumbel_kernel<true>, dim3(num_rows), dim3(kSampThreads), 0, stream, logits,
+                           row_stride, temperatures, noise, noise_row_stride, k0, k1, o0, o1, tokens, vocab);
+    else
+        hipLaunchKernelGGL(sample_gumbel_kernel<false>, dim3(num_rows), dim3(kSampThreads), 0, stream, logits,
+                           row_stride, temperatures, noise, noise_row_stride, k0, k1, o0, o1, tokens, vocab);
+    return hipGetLastError();
+}
+
+}  // namespace pkv

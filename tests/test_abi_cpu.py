@@ -190,3 +190,29 @@ def test_decode_graph_validation(lib):
     assert lib.pkv_decode_graph_bucket(None, 3) == -1
     assert lib.pkv_decode_graph_launch(None, 3, None) == -1
     lib.pkv_decode_graph_destroy(None)
+
+
+def test_sublayer_ops_validation(lib):
+    R = ctypes.c_void_p(0x2000)
+    f = lib.pkv_add_rms_norm
+    assert f(FAKE, R, FAKE, FAKE, ctypes.c_void_p(0x4000), 4, 4100, 1e-6, None) == -1       # hidden % 8
+    assert f(FAKE, R, FAKE, FAKE, ctypes.c_void_p(0x4000), 4, 32768, 1e-6, None) == -2      # above 16384
+    assert f(FAKE, R, FAKE, FAKE, None, 4, 4096, 1e-6, None) == -1                          # residual without output
+    assert f(FAKE, None, FAKE, FAKE, R, 4, 4096, 1e-6, None) == -1                          # output without residual
+    assert f(FAKE, R, FAKE, R, R, 4, 4096, 1e-6, None) == -1 and "differ" in _err(lib)       # y == residual_out
+    assert f(ctypes.c_void_p(0x1008), R, FAKE, FAKE, ctypes.c_void_p(0x4000), 4, 4096, 1e-6, None) == -1
+    assert f(None, None, None, None, None, 0, 4096, 1e-6, None) == 0                         # empty
+    g = lib.pkv_silu_and_mul
+    assert g(FAKE, 24576, R, 12288, 4, 12300, None) == -1                                    # intermediate % 8
+    assert g(FAKE, 12288, R, 12288, 4, 12288, None) == -1                                    # x rows too short
+    assert g(FAKE, 24576, R, 12280, 4, 12288, None) == -1                                    # out rows too short
+    assert g(FAKE, 24576, None, 12288, 4, 12288, None) == -1
+    assert g(None, 24576, None, 12288, 0, 12288, None) == 0
+    h = lib.pkv_sample_gumbel
+    T, TOK = ctypes.c_void_p(0x5000), ctypes.c_void_p(0x6000)
+    assert h(FAKE, 151936, 2, T, None, 0, 1, 0, TOK, 4, 151936, None) == -2                  # dtype
+    assert h(FAKE, 151930, 0, T, None, 0, 1, 0, TOK, 4, 151936, None) == -1                  # stride < vocab
+    assert h(FAKE, 151939, 0, T, None, 0, 1, 0, TOK, 4, 151936, None) == -1                  # bf16 stride % 8
+    assert h(FAKE, 151936, 0, T, R, 151935, 1, 0, TOK, 4, 151936, None) == -1                # noise stride
+    assert h(FAKE, 151936, 0, None, None, 0, 1, 0, TOK, 4, 151936, None) == -1               # temperatures
+    assert h(None, 151936, 0, None, None, 0, 1, 0, None, 0, 151936, None) == 0               # no rows
