@@ -223,12 +223,14 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
         // s[kh][r] = raw score of key j0 + 32kh + 8(r/4) + 4*h32 + r%4 for query qi.
         const bool need_mask = !ok || (j0 + kKT - 1 > off + wp0) || (j0 + kKT > Lk);
         if (need_mask) {
+            // key j0 + 4*h32 + c (c a compile-time offset) is visible iff c <= lim
+            const int lim = ok ? min(qpos, Lk - 1) - (j0 + 4 * h32) : -1;
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int kp = j0 + 32 * kh + 8 * (r >> 2) + 4 * h32 + (r & 3);
-                    s[kh][r] = (!ok || kp > qpos || kp >= Lk) ? -INFINITY : s[kh][r];
+                    const int c = 32 * kh + 8 * (r >> 2) + (r & 3);
+                    s[kh][r] = c > lim ? -INFINITY : s[kh][r];
                 }
         }
         float tmax = -INFINITY;
@@ -236,7 +238,11 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) tmax = __builtin_fmaxf(__builtin_fmaxf(tmax, s[kh][r]), s[kh][r + 1]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        {
+            // exchange with the lane 32 away without an LDS round trip (v_permlane32_swap)
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+            tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
         // Lazy reference max (raw score units): it moves only when a row's max grows
         // by more than 2^kLazyLog2 in the exponent, so the weights stay <= 256 and the
         // O rescale is skipped on most tiles.  Exact: O and l share the reference.
