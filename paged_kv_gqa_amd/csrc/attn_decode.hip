@@ -10,22 +10,24 @@
 //
 // Design (HBM-bound: every K/V byte of the context is read once):
 //   * Split-K: a workgroup owns (sequence b, kv head g, split s) and covers
-//     `split_blocks` consecutive logical 256-token blocks; the whole GQA group
-//     of q heads is served by one read of K/V.
+//     up to 16 consecutive logical 256-token blocks; the whole GQA group of q
+//     heads is served by one read of K/V.  The last splits (which exist only
+//     for the longest contexts, and are full) are dispatched first.
 //   * Inside the workgroup each of the 4 waves streams its own 16-key slice
 //     of every 64-key quarter block and keeps its own online-softmax state, so
-//     the main loop has no workgroup barrier at all.  Loads run ahead in a
-//     ring of registers, so a wave keeps several 8 KB chunks of K/V in flight
-//     while it computes.
-//   * QK^T on MFMA (v_mfma_f32_16x16x32_bf16): A = 16 keys x 32 dims straight
-//     from global memory, B = the group's q vectors (columns >= G are zero).
-//   * The running max is rescaled lazily: the reference max only moves when a
-//     chunk's max exceeds it by more than 2^8 (the weights stay <= 256 in
-//     fp32), so the common chunk needs no cross-lane max exchange.  The result
-//     is exact: numerator and denominator share the reference.
-//   * Probabilities reach the PV lanes through a wave-private LDS slot; PV runs
-//     on the vector ALU with each lane owning 8 dims of 4 keys (fully
-//     coalesced 256-byte V rows).
+//     the main loop has no workgroup barrier at all.  Loads run one chunk
+//     ahead in a register ring.
+//   * Both products on MFMA.  Scores: v_mfma_f32_16x16x32_bf16 with A = 16 keys
+//     x 32 dims straight from global memory and B = the group's q vectors
+//     (columns >= G are zero); a lane then holds 4 keys of one head column.
+//     That layout is already the B operand of P V on v_mfma_f32_16x16x16_bf16,
+//     so the probabilities never leave registers; the A operand V^T comes from
+//     the chunk's V rows staged in a wave-private LDS tile and read back with
+//     the gfx950 transposing LDS read (ds_read_b64_tr_b16).
+//   * Every softmax statistic is lane-local (a lane's column is one head).  The
+//     running max is rescaled lazily: the reference only moves when a chunk's
+//     max exceeds it by more than 2^8 (the weights stay <= 256 in fp32).  The
+//     result is exact: numerator and denominator share the reference.
 //   * Keys at or past the context length and keys of a block id outside the
 //     pool are masked before the exponential and their V rows replaced by
 //     zeros, so nothing outside the context can reach the output.
@@ -39,26 +41,23 @@ namespace pkv {
 
 namespace {
 constexpr int kDecThreads = 256;
+// Tuning (measured on MI355X, Qwen3-8B decode workload): splits of up to 16
+// blocks, a ring of 2 chunks of 16 keys per wave, 2 waves per SIMD.  Longer
+// splits amortise each workgroup's pipeline fill; deeper rings did not pay.
 #ifndef PKV_DECODE_SPLIT
-#define PKV_DECODE_SPLIT 4
+#define PKV_DECODE_SPLIT 16
 #endif
-constexpr int kMaxSplitBlocks = PKV_DECODE_SPLIT;   // blocks per split-K work item (at most)
-constexpr int kTargetItems = 4096;
-constexpr float kLazyMax = 8.0f;   // log2 headroom of the lazy reference max
-// Tuning (measured on MI355X, Qwen3-8B decode workload): a ring of 3 chunks of 16
-// keys per wave at 2 waves/SIMD, 4-block splits, launched split-index-slowest.
 #ifndef PKV_DECODE_DEPTH
-#define PKV_DECODE_DEPTH 3
+#define PKV_DECODE_DEPTH 2
 #endif
 #ifndef PKV_DECODE_OCC
 #define PKV_DECODE_OCC 2
 #endif
-#ifndef PKV_DECODE_CHUNK
-#define PKV_DECODE_CHUNK 16
-#endif
+constexpr int kMaxSplitBlocks = PKV_DECODE_SPLIT;   // blocks per split-K work item (at most)
+constexpr int kTargetItems = 4096;
+constexpr float kLazyMax = 8.0f;   // log2 headroom of the lazy reference max
 constexpr int kDepth = PKV_DECODE_DEPTH;   // register ring: chunks in flight + the one computed
-constexpr int kCK = PKV_DECODE_CHUNK;      // keys per wave per chunk (16 or 32)
-constexpr int kTiles = kCK / 16;           // 16-key MFMA tiles per chunk
+constexpr int kCK = 16;                    // keys per wave per chunk (one 16-key MFMA tile)
 constexpr int kRounds = kBlockSize / (4 * kCK);  // chunks per 256-token block per wave
 constexpr int kOcc = PKV_DECODE_OCC;       // waves per SIMD the register budget is sized for
 
@@ -77,9 +76,10 @@ inline Workspace carve(void* base, int32_t B, int32_t hq, int32_t max_splits) {
     return w;
 }
 
+typedef short short4_t __attribute__((ext_vector_type(4)));
 struct Chunk {
-    u32x4 k[kTiles][4];   // MFMA A operand: key 16*t + lane%16, dims 8*(lane/16) + 32*st
-    u32x4 v[kCK / 4];     // PV: key lane/16 + 4*i, dims 8*(lane%16)
+    u32x4 k[4];           // score A operand: key lane%16, dims 8*(lane/16) + 32*st
+    u32x4 v[kCK / 4];     // V rows: key lane/16 + 4*i, dims 8*(lane%16) (staged through LDS)
 };
 }  // namespace
 
@@ -108,9 +108,9 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
     int32_t hq, int32_t hkv, int64_t num_blocks, float scale_log2, int32_t split_blocks, int32_t max_splits,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
     static_assert(G >= 1 && G <= 16, "GQA group must fit the 16 MFMA columns");
-    // Split index slowest: every sequence's first splits are dispatched before any
-    // later split, so the empty workgroups past short contexts trail the real work.
-    const int g = blockIdx.x, b = blockIdx.y, s = blockIdx.z;
+    // The last splits are dispatched first: they exist only for the longest
+    // contexts and are full, so the short first splits fill the tail.
+    const int g = blockIdx.x, b = blockIdx.y, s = (int)gridDim.z - 1 - (int)blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     int ctx = context_lens[b];
@@ -119,10 +119,11 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
     const int nblk = (ctx + kBlockSize - 1) / kBlockSize;
     const int blk0 = s * split_blocks;
     if (blk0 >= nblk) return;
-    const int nb = min(split_blocks, nblk - blk0);   // blocks of this split (<= 16)
-    const int nchunks = nb * kRounds;                // chunks of 4*kCK keys; this wave owns kCK of each
+    const int nb = min(split_blocks, nblk - blk0);   // blocks of this split
+    const int nchunks = nb * kRounds;                // chunks of 64 keys; this wave owns 16 of each
 
-    __shared__ float s_p[4][kCK][G];                 // per-wave probabilities of one chunk
+    constexpr int kVPitch = kHeadDim * 2 + 32;       // bytes per V row in LDS (conflict-free transposed reads)
+    __shared__ __attribute__((aligned(16))) unsigned char s_v[4][kCK * kVPitch];   // per-wave V tile
     __shared__ float s_m[4][G], s_l[4][G];           // per-wave final max / sum
     __shared__ float s_o[4][G][kHeadDim];            // per-wave final numerators
 
@@ -135,8 +136,9 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
         my_blk = (id >= 0 && (int64_t)id < num_blocks) ? id : -1;
     }
 
-    // B operand: q of head g*G + col, dims 8*(lane/16) + 32*st .. +7, zero for col >= G.
+    // Lane (col, grp): col = head column of both products, grp = 4-key group.
     const int col = lane & 15, grp = lane >> 4;
+    // B operand of the scores: q of head g*G + col, dims 8*grp + 32*st .. +7, zero for col >= G.
     bf16x8 qb[4];
     {
         const bool on = col < G;
@@ -148,113 +150,79 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
         }
     }
 
-    // Chunk j covers keys kCK*(4*(j%kRounds) + wave) .. +kCK-1 of block blk0 + j/kRounds.
+    // Chunk j covers keys 16*(4*(j%kRounds) + wave) .. +15 of block blk0 + j/kRounds.
     auto block_of = [&](int j) { return __builtin_amdgcn_readlane(my_blk, j / kRounds); };
     auto chunk_row0 = [&](int j) { return kCK * (4 * (j % kRounds) + wave); };
     auto load = [&](Chunk& c, int j) {
         const int id = block_of(j);
         const int64_t phys = id < 0 ? 0 : id;
         const int64_t r0 = phys * kBlockSize + chunk_row0(j);   // first cache row of the chunk
+        // K as the A operand: key col, dims 8*grp + 32*st
+        const uint16_t* kp = k_cache + (r0 + col) * row + (int64_t)g * kHeadDim + 8 * grp;
 #pragma unroll
-        for (int t = 0; t < kTiles; ++t) {
-            const uint16_t* kp = k_cache + (r0 + 16 * t + col) * row + (int64_t)g * kHeadDim + 8 * grp;
-#pragma unroll
-            for (int st = 0; st < 4; ++st)
-                c.k[t][st] = ldg128(kp + 32 * st);
-        }
+        for (int st = 0; st < 4; ++st) c.k[st] = ldg128(kp + 32 * st);
         __builtin_amdgcn_sched_barrier(0);   // K before V: the scores wait only for K
+        // V rows: key grp + 4*i, dims 8*col .. +7 (staged through LDS for the transposed read)
         const uint16_t* vp = v_cache + (r0 + grp) * row + (int64_t)g * kHeadDim + 8 * col;
 #pragma unroll
-        for (int i = 0; i < kCK / 4; ++i)
-            c.v[i] = ldg128(vp + (int64_t)(4 * i) * row);
+        for (int i = 0; i < kCK / 4; ++i) c.v[i] = ldg128(vp + (int64_t)(4 * i) * row);
     };
 
-    float m_head[G];                  // lazy reference max per head (wave-uniform)
+    float m_ref = -INFINITY;          // lazy reference max of column col (log2 units)
+    float l_run = 0.f;                // this lane's share of column col's sum
+    f32x4 acc[8];                     // O^T tile d: dims 16d + 4*grp + r, column col
 #pragma unroll
-    for (int h = 0; h < G; ++h) m_head[h] = -INFINITY;
-    float l_run = 0.f;                // lanes col < G: running sum of their keys' weights
-    float acc[G][8];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    for (int d = 0; d < 8; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    unsigned char* vt = s_v[wave];
+    typedef __attribute__((address_space(3))) bf16x4* lds4_t;
 
     auto compute = [&](const Chunk& c, int j) {
         const int key0 = (blk0 + j / kRounds) * kBlockSize + chunk_row0(j);
         const int id = block_of(j);
-        // ---- scores: tile t holds 16 keys x 16 columns
-        float sv[kTiles][4];
+        // ---- V rows into this wave's LDS tile; keys outside the context become zeros
+#pragma unroll
+        for (int i = 0; i < kCK / 4; ++i) {
+            const bool live = id >= 0 && (key0 + grp + 4 * i) < ctx;
+            *reinterpret_cast<u32x4*>(vt + (grp + 4 * i) * kVPitch + 16 * col) =
+                live ? c.v[i] : u32x4{0u, 0u, 0u, 0u};
+        }
+        // ---- scores S[key][col] on MFMA: lane holds keys 4*grp + r of column col
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c.k[st]), qb[st], sc, 0, 0, 0);
+        float sv[4];
         float mx = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < kTiles; ++t) {
-            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int st = 0; st < 4; ++st)
-                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c.k[t][st]), qb[st], sc, 0, 0,
-                                                             0);
-            // sc[r] = score of key key0 + 16t + 4*grp + r for column col
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = key0 + 16 * t + 4 * grp + r;
-                sv[t][r] = (id >= 0 && key < ctx) ? sc[r] * scale_log2 : -INFINITY;
-                mx = fmaxf(mx, sv[t][r]);
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int key = key0 + 4 * grp + r;
+            sv[r] = (id >= 0 && key < ctx) ? sc[r] * scale_log2 : -INFINITY;
+            mx = fmaxf(mx, sv[r]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        // ---- lazy reference: a head's reference moves only when this chunk's max
-        // exceeds it by more than 2^kLazyMax.  Branch-free: the per-head maxima are
-        // read into wave-uniform registers and alpha is 1 when nothing moves.
-        float ref = 0.f, my_alpha = 1.f;
+        // ---- lazy reference, lane-local (every lane of a column holds the same max)
+        const float mn = (mx > m_ref + kLazyMax) ? mx : m_ref;
+        const float alpha = m_ref == -INFINITY ? 0.f : exp2f(m_ref - mn);
+        m_ref = mn;
+        const float ref = mn == -INFINITY ? 0.f : mn;
+        float p[4];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), h));
-            const float mold = m_head[h];
-            const float mn = (mh > mold + kLazyMax) ? mh : mold;
-            const float alpha = mold == -INFINITY ? 0.f : exp2f(mold - mn);
-            m_head[h] = mn;
+        for (int r = 0; r < 4; ++r) p[r] = exp2f(sv[r] - ref);
+        l_run = fmaf(l_run, alpha, (p[0] + p[1]) + (p[2] + p[3]));
+        // B operand of P V: keys 4*grp + r of column col -- the score layout itself
+        const bf16x4 pb = {(bf16)p[0], (bf16)p[1], (bf16)p[2], (bf16)p[3]};
+        // ---- O^T += V^T P on MFMA; V^T tiles by transposing LDS reads: lane j of the
+        // 16-lane group grp addresses key 4*grp + j/4, dims 16d + 4*(j%4) and receives
+        // dim 16d + j across those 4 keys.
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
-            if (col == h) {
-                my_alpha = alpha;
-                ref = mn == -INFINITY ? 0.f : mn;
-            }
+        for (int d = 0; d < 8; ++d) {
+            const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds4_t)(vt + (4 * grp + (col >> 2)) * kVPitch + 2 * (16 * d + 4 * (col & 3))));
+            acc[d] *= alpha;
+            acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, va),
+                                                                __builtin_bit_cast(short4_t, pb), acc[d], 0, 0, 0);
         }
-        l_run *= my_alpha;
-        if (col < G) {
-#pragma unroll
-            for (int t = 0; t < kTiles; ++t)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float p = exp2f(sv[t][r] - ref);
-                    l_run += p;
-                    s_p[wave][16 * t + 4 * grp + r][col] = p;
-                }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // ---- PV: this lane owns dims 8*col .. +7 of keys grp + 4*i
-#pragma unroll
-        for (int i = 0; i < kCK / 4; ++i) {
-            const int kl = grp + 4 * i;
-            const bool live = id >= 0 && (key0 + kl) < ctx;
-            const u32x4 w = live ? c.v[i] : u32x4{0u, 0u, 0u, 0u};
-            float vv[8];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                vv[2 * x] = bf16lo(w[x]);
-                vv[2 * x + 1] = bf16hi(w[x]);
-            }
-            float p[G];
-#pragma unroll
-            for (int h = 0; h < G; ++h) p[h] = s_p[wave][kl][h];
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p[h], vv[e], acc[h][e]);
-        }
-        __builtin_amdgcn_wave_barrier();   // s_p is rewritten by the next chunk
     };
 
     // ---- main loop: kDepth - 1 chunks in flight while one is computed.  Every
@@ -282,26 +250,14 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
     if (lane < G) {
-        float mh = m_head[0];
-#pragma unroll
-        for (int h = 1; h < G; ++h) mh = (lane == h) ? m_head[h] : mh;
-        s_m[wave][lane] = mh;
+        s_m[wave][lane] = m_ref;
         s_l[wave][lane] = lsum;
     }
+    if (col < G) {
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+        for (int d = 0; d < 8; ++d)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float v = acc[h][e];
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
-            acc[h][e] = v;
-        }
-    if (grp == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s_o[wave][h][8 * col + e] = acc[h][e];
+            for (int r = 0; r < 4; ++r) s_o[wave][col][16 * d + 4 * grp + r] = acc[d][r];
     }
     __syncthreads();
     const int64_t bh0 = (int64_t)b * hq + (int64_t)g * G;
