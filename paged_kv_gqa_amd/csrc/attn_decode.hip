@@ -11,8 +11,10 @@
 // Design (HBM-bound: every K/V byte of the context is read once):
 //   * Split-K: a workgroup owns (sequence b, kv head g, split s) and covers
 //     up to 16 consecutive logical 256-token blocks; the whole GQA group of q
-//     heads is served by one read of K/V.  The last splits (which exist only
-//     for the longest contexts, and are full) are dispatched first.
+//     heads is served by one read of K/V.  A one-workgroup kernel first sorts
+//     the split items by size (counting sort), and workgroups take them largest
+//     first: with contexts of very different lengths the last workgroups to
+//     start are the smallest, so the tail stays short.
 //   * Inside the workgroup each of the 4 waves streams its own 16-key slice
 //     of every 64-key quarter block and keeps its own online-softmax state, so
 //     the main loop has no workgroup barrier at all.  Loads run one chunk
@@ -64,6 +66,7 @@ constexpr int kOcc = PKV_DECODE_OCC;       // waves per SIMD the register budget
 struct Workspace {
     float* part_o;   // [B][Hq][S][128]
     float* part_ml;  // [B][Hq][S][2]
+    int32_t* work;   // [S][B] split items b * S + s, largest first (dispatch order)
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -71,8 +74,10 @@ __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size
 inline Workspace carve(void* base, int32_t B, int32_t hq, int32_t max_splits) {
     Workspace w;
     const size_t o_bytes = align256((size_t)B * hq * max_splits * kHeadDim * sizeof(float));
+    const size_t ml_bytes = align256((size_t)B * hq * max_splits * 2 * sizeof(float));
     w.part_o = (float*)base;
     w.part_ml = (float*)((char*)base + o_bytes);
+    w.work = (int32_t*)((char*)base + o_bytes + ml_bytes);
     return w;
 }
 
@@ -98,7 +103,8 @@ size_t decode_workspace_bytes(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t
     const int64_t ms = (max_blocks + sb - 1) / sb;
     const size_t o_bytes = align256((size_t)num_seqs * hq * ms * kHeadDim * sizeof(float));
     const size_t ml_bytes = align256((size_t)num_seqs * hq * ms * 2 * sizeof(float));
-    return o_bytes + ml_bytes;
+    const size_t work_bytes = align256((size_t)num_seqs * ms * sizeof(int32_t));
+    return o_bytes + ml_bytes + work_bytes;
 }
 
 template <int G>
@@ -106,11 +112,12 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ block_table, int32_t max_blocks,
     int32_t hq, int32_t hkv, int64_t num_blocks, float scale_log2, int32_t split_blocks, int32_t max_splits,
-    float* __restrict__ part_o, float* __restrict__ part_ml) {
+    float* __restrict__ part_o, float* __restrict__ part_ml, const int32_t* __restrict__ work) {
     static_assert(G >= 1 && G <= 16, "GQA group must fit the 16 MFMA columns");
-    // The last splits are dispatched first: they exist only for the longest
-    // contexts and are full, so the short first splits fill the tail.
-    const int g = blockIdx.x, b = blockIdx.y, s = (int)gridDim.z - 1 - (int)blockIdx.z;
+    // Dispatch order: split items by decreasing size (full splits first), so the
+    // smallest pieces of work come last and the tail stays short.
+    const int item = work[(int64_t)blockIdx.z * gridDim.y + blockIdx.y];
+    const int g = blockIdx.x, b = item / max_splits, s = item - b * max_splits;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     int ctx = context_lens[b];
@@ -283,6 +290,40 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
     }
 }
 
+// Dispatch order of the split items (b, s): a counting sort by the number of
+// blocks the item covers, largest first, empty items last (one workgroup; items
+// of equal size in any order -- the order only schedules work, every result is
+// the same).
+__global__ void __launch_bounds__(1024) decode_order_kernel(const int32_t* __restrict__ context_lens,
+                                                            int32_t max_blocks, int32_t num_seqs, int32_t split_blocks,
+                                                            int32_t max_splits, int32_t* __restrict__ work) {
+    __shared__ int32_t s_bin[kMaxSplitBlocks + 1];
+    const int tid = threadIdx.x;
+    const int cap = max_blocks * kBlockSize;
+    const int n_items = num_seqs * max_splits;
+    auto key = [&](int it) {   // split_blocks - (blocks of the item): 0 = full
+        const int b = it / max_splits, s = it - b * max_splits;
+        int ctx = context_lens[b];
+        ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+        const int nb = (ctx + kBlockSize - 1) / kBlockSize - s * split_blocks;
+        return split_blocks - (nb < 0 ? 0 : (nb > split_blocks ? split_blocks : nb));
+    };
+    if (tid <= split_blocks) s_bin[tid] = 0;
+    __syncthreads();
+    for (int it = tid; it < n_items; it += 1024) atomicAdd(&s_bin[key(it)], 1);
+    __syncthreads();
+    if (tid == 0) {   // exclusive prefix over the bins
+        int run = 0;
+        for (int i = 0; i <= split_blocks; ++i) {
+            const int c = s_bin[i];
+            s_bin[i] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    for (int it = tid; it < n_items; it += 1024) work[atomicAdd(&s_bin[key(it)], 1)] = it;
+}
+
 // One workgroup of 128 threads per (b, h): merge the splits in order.  The
 // splits are taken 128 at a time: their (m, l) pairs are loaded by the whole
 // workgroup at once and their weights exp2(m_s - M) staged in LDS, then each
@@ -341,12 +382,15 @@ hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t stream) {
     const int sb = decode_split_blocks(a.num_seqs, a.hkv, a.max_blocks);
     const int ms = (a.max_blocks + sb - 1) / sb;
     Workspace w = carve(a.workspace, a.num_seqs, a.hq, ms);
+    hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(1024), 0, stream, a.context_lens, a.max_blocks, a.num_seqs,
+                       sb, ms, w.work);
     dim3 grid(a.hkv, a.num_seqs, ms);
 #define PKV_DECODE_CASE(GG)                                                                                       \
     case GG:                                                                                                      \
         hipLaunchKernelGGL(decode_split_kernel<GG>, grid, dim3(kDecThreads), 0, stream, (const uint16_t*)a.q,     \
                            (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.context_lens, a.block_table, \
-                           a.max_blocks, a.hq, a.hkv, a.num_blocks, a.scale_log2, sb, ms, w.part_o, w.part_ml);   \
+                           a.max_blocks, a.hq, a.hkv, a.num_blocks, a.scale_log2, sb, ms, w.part_o, w.part_ml,   \
+                           w.work);                                                                               \
         break;
     switch (G) {
         PKV_DECODE_CASE(1)
