@@ -214,7 +214,7 @@ def _prefill_case(dev, lens_q, lens_k, hq, hkv, seed, paged=False, num_blocks=No
     return o, ref, (q, kc, vc, cuq, cuk, bt)
 
 
-@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 8), (8, 8)])
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 8), (8, 8), (64, 8), (4, 2)])
 def test_prefill_varlen_ragged(dev, hq, hkv):
     lens = [1, 37, 63, 64, 65, 129, 300]
     _say(f"prefill case 1, lengths {lens}, {hq}/{hkv} heads")
@@ -348,7 +348,7 @@ def _decode_case(dev, ctx, hq, hkv, seed, nan_canaries=False, permute=False):
     return out
 
 
-@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 8), (8, 8)])
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 8), (8, 8), (64, 8), (128, 8)])
 def test_decode_small_ragged(dev, hq, hkv):
     ctx = [1, 2, 255, 256, 257, 300, 1000, 4097, 0]
     _say(f"decode contexts {ctx}, {hq}/{hkv} heads, NaN canaries, permuted pool")
@@ -365,6 +365,29 @@ def test_decode_long_context_many_splits(dev):
     _say(f"decode long contexts {ctx}")
     r = _decode_case(dev, ctx, 32, 8, seed=11)
     check_attn(f64(r["o"]), r["ref"], "decode long")
+
+
+def test_decode_large_batch_short_contexts(dev):
+    """1500 sequences: the split-item sort and the grid loop over more items than threads."""
+    rng = wl.rng_for(97, 0, 0)
+    ctx = [int(c) for c in rng.integers(0, 700, size=1500)]
+    ctx[:3] = [0, 1, 699]
+    _say("decode 1500 sequences, contexts 0..699, 32/8 heads")
+    r = _decode_case(dev, ctx, 32, 8, seed=21)
+    got = f64(r["o"])
+    live = np.array(ctx) > 0
+    check_attn(got[live], r["ref"][live], "decode large batch")
+    assert np.all(got[~live] == 0.0)
+
+
+def test_prefill_long_paged_chunk(dev):
+    """A 300-query chunk at the end of a 40960-token context (the largest position), paged."""
+    _say("prefill: 300 queries over 40960 paged keys, sampled rows")
+    rng = np.random.default_rng(5)
+    rows = np.stack([rng.integers(0, 300, 48), rng.integers(0, 32, 48)], 1)
+    rows[:2] = [[0, 0], [299, 31]]
+    o, ref, _ = _prefill_case(dev, [300], [40960], 32, 8, seed=23, paged=True, rows=rows)
+    check_attn(f64(o)[rows[:, 0], rows[:, 1]], ref, "prefill long chunk")
 
 
 def _pool_workload(dev, w):
