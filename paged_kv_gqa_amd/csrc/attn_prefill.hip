@@ -18,9 +18,10 @@
 //     and the sum stay in registers; only the max needs one swap with the
 //     lane 32 away.  The S^T accumulator is, after exp2 and bf16 packing,
 //     already the B operand of the PV product.
-//   * A workgroup (4 waves, 32 query rows each) owns one kv head and the
-//     query heads of its GQA group that share it, so each K/V tile staged in
-//     LDS feeds 128 query rows.  K and V are both kept row-major in LDS
+//   * A workgroup owns one kv head and the query heads of its GQA group that
+//     share it; each wave computes 32 query rows of one head.  With groups of
+//     4 the workgroup has 8 waves (4 heads x 64 positions) and each K/V tile
+//     staged in LDS feeds 256 query rows; smaller groups use 4 waves.  K and V are both kept row-major in LDS
 //     (plain 16-byte copies, padded rows: no bank conflicts); the PV product
 //     needs V transposed, which the gfx950 transposing LDS read
 //     (ds_read_b64_tr_b16) delivers: lane j of a 16-lane group addresses key
@@ -45,8 +46,6 @@ namespace pkv {
 
 namespace {
 typedef __attribute__((address_space(3))) bf16x4* lds_ptr_t;
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
 constexpr int kKT = 64;                    // keys per tile
 constexpr int kKPitch = kHeadDim * 2 + 16;  // bytes per K row in LDS (row-major)
@@ -56,10 +55,15 @@ constexpr int kVTileBytes = kKT * kVPitch;
 constexpr float kLazyLog2 = 8.0f;           // the lazy reference max moves when a row grows by > 2^8
 }  // namespace
 
-template <int GW, bool PAGED>
-__global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int32_t m_blocks, int32_t n_work,
-                                                              int32_t head_groups) {
-    constexpr int kPosSub = kWaves / GW;                // position sub-blocks per workgroup
+// NW waves per workgroup (4 or 8); two waves per SIMD either way (two
+// workgroups of 4 per CU, or one of 8).
+template <int GW, bool PAGED, int NW>
+__global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a, int32_t m_blocks, int32_t n_work,
+                                                                  int32_t head_groups) {
+    constexpr int kThreads = 64 * NW;
+    constexpr int kLoadRows = kThreads / 16;            // tile rows one sweep of 16-byte pieces covers
+    constexpr int kLoadIters = kKT / kLoadRows;         // sweeps per 64-row tile
+    constexpr int kPosSub = NW / GW;                    // position sub-blocks per workgroup
     constexpr int kBM = kRowsPerWave * kPosSub;         // query positions per workgroup
     __shared__ __attribute__((aligned(16))) unsigned char k_lds[2 * kKTileBytes];
     __shared__ __attribute__((aligned(16))) unsigned char v_lds[2 * kVTileBytes];
@@ -115,8 +119,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
     float m_run = -INFINITY, l_part = 0.f;      // running reference max (raw units), partial sum
     const float lazy_raw = kLazyLog2 / a.scale_log2;
 
-    // ---- tile loader.  Thread tid moves 16-byte piece tid%16 of rows tid/16 + 16*i
-    // (i < 4) of the 64-row K and V tiles.  Row offsets are loop-invariant; every
+    // ---- tile loader.  Thread tid moves 16-byte piece tid%16 of rows tid/16 + kLoadRows*i
+    // (i < kLoadIters) of the 64-row K and V tiles.  Row offsets are loop-invariant; every
     // load is issued on every path (rows past the last key are clamped onto it), so
     // the compiler's wait counts stay exact.
     const int64_t krs = a.k_row_stride, vrs = a.v_row_stride;
@@ -124,11 +128,11 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
     const uint16_t* vbase = (const uint16_t*)a.v + (int64_t)g * kHeadDim;
     const int32_t* bt = PAGED ? a.block_table + (int64_t)b * a.max_blocks : nullptr;
     const int lrow = tid >> 4, piece = tid & 15;
-    int64_t koff[4], voff[4];
+    int64_t koff[kLoadIters], voff[kLoadIters];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        koff[i] = (int64_t)(lrow + 16 * i) * krs + piece * 8;
-        voff[i] = (int64_t)(lrow + 16 * i) * vrs + piece * 8;
+    for (int i = 0; i < kLoadIters; ++i) {
+        koff[i] = (int64_t)(lrow + kLoadRows * i) * krs + piece * 8;
+        voff[i] = (int64_t)(lrow + kLoadRows * i) * vrs + piece * 8;
     }
     // First cache/array row of tile t and whether its block id is usable (tiles
     // never straddle a 256-token block).
@@ -144,7 +148,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
             return (int64_t)ck0 + j0;
         }
     };
-    u32x4 kst[4], vst[4];
+    u32x4 kst[kLoadIters], vst[kLoadIters];
     auto load_tile = [&](int t) {
         bool ok;
         const int64_t r0 = tile_row0(t, ok);
@@ -153,19 +157,19 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
             const uint16_t* kp = kbase + r0 * krs;
             const uint16_t* vp = vbase + r0 * vrs;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) kst[i] = ldg128(kp + koff[i]);
+            for (int i = 0; i < kLoadIters; ++i) kst[i] = ldg128(kp + koff[i]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) vst[i] = ldg128(vp + voff[i]);
+            for (int i = 0; i < kLoadIters; ++i) vst[i] = ldg128(vp + voff[i]);
         } else {
             // partial or unusable tile: clamp rows onto valid memory, zero V at store time
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t row = r0 + (ok ? min(lrow + 16 * i, last) : 0);
+            for (int i = 0; i < kLoadIters; ++i) {
+                const int64_t row = r0 + (ok ? min(lrow + kLoadRows * i, last) : 0);
                 kst[i] = ldg128(kbase + row * krs + piece * 8);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t row = r0 + (ok ? min(lrow + 16 * i, last) : 0);
+            for (int i = 0; i < kLoadIters; ++i) {
+                const int64_t row = r0 + (ok ? min(lrow + kLoadRows * i, last) : 0);
                 vst[i] = ldg128(vbase + row * vrs + piece * 8);
             }
         }
@@ -178,13 +182,13 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
             // V rows of keys past the end (or of an unusable block) become zeros, so
             // whatever those cache slots hold cannot reach the output through P V.
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (!ok || lrow + 16 * i > last) vst[i] = u32x4{0u, 0u, 0u, 0u};
+            for (int i = 0; i < kLoadIters; ++i)
+                if (!ok || lrow + kLoadRows * i > last) vst[i] = u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<u32x4*>(kb + (lrow + 16 * i) * kKPitch + piece * 16) = kst[i];
-            *reinterpret_cast<u32x4*>(vb + (lrow + 16 * i) * kVPitch + piece * 16) = vst[i];
+        for (int i = 0; i < kLoadIters; ++i) {
+            *reinterpret_cast<u32x4*>(kb + (lrow + kLoadRows * i) * kKPitch + piece * 16) = kst[i];
+            *reinterpret_cast<u32x4*>(vb + (lrow + kLoadRows * i) * kVPitch + piece * 16) = vst[i];
         }
     };
 
@@ -325,22 +329,25 @@ hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t stream) {
     const int gw = G >= 4 ? 4 : G;                 // query heads per workgroup
     if (G % gw) return hipErrorInvalidValue;
     const int head_groups = G / gw;
-    const int bm = kRowsPerWave * (kWaves / gw);
+    // Four query heads share each K/V tile across 8 waves (64 positions); smaller
+    // groups keep 4 waves so short sequences still spread over many workgroups.
+    const int nw = gw == 4 ? 8 : 4;
+    const int bm = kRowsPerWave * (nw / gw);
     const int m_blocks = (a.max_seqlen_q + bm - 1) / bm;
     const int64_t n_work64 = (int64_t)a.num_seqs * a.hkv * head_groups * m_blocks;
     if (n_work64 > (int64_t)0x7FFFFFF0) return hipErrorInvalidValue;
     const int n_work = (int)n_work64;
     const int grid = ((n_work + 7) / 8) * 8;
     const bool paged = a.block_table != nullptr;
-#define PKV_PREFILL(GW_, PG_)                                                                                  \
-    hipLaunchKernelGGL((prefill_kernel<GW_, PG_>), dim3(grid), dim3(kThreads), 0, stream, a, m_blocks, n_work, \
+#define PKV_PREFILL(GW_, PG_, NW_)                                                                               \
+    hipLaunchKernelGGL((prefill_kernel<GW_, PG_, NW_>), dim3(grid), dim3(64 * NW_), 0, stream, a, m_blocks, n_work, \
                        head_groups)
     if (gw == 4) {
-        if (paged) PKV_PREFILL(4, true); else PKV_PREFILL(4, false);
+        if (paged) PKV_PREFILL(4, true, 8); else PKV_PREFILL(4, false, 8);
     } else if (gw == 2) {
-        if (paged) PKV_PREFILL(2, true); else PKV_PREFILL(2, false);
+        if (paged) PKV_PREFILL(2, true, 4); else PKV_PREFILL(2, false, 4);
     } else if (gw == 1) {
-        if (paged) PKV_PREFILL(1, true); else PKV_PREFILL(1, false);
+        if (paged) PKV_PREFILL(1, true, 4); else PKV_PREFILL(1, false, 4);
     } else {
         return hipErrorInvalidValue;
     }
