@@ -493,3 +493,23 @@ def test_decode_row_equals_prefill_row(dev):
     torch.cuda.synchronize()
     err = np.abs(f64(od) - f64(o)[last])
     assert err.max() <= 2e-2, err.max()
+
+
+def test_decode_unusable_block_ids_drop_their_keys(dev):
+    """A block id of -1 or past the pool inside the context: its keys are never read and
+    drop out of the softmax (the documented behaviour for invalid metadata).  With the
+    bad id in the last block, the result is attention over the keys before it."""
+    _say("decode with -1 / out-of-pool block ids in the last block of the context")
+    rng = wl.rng_for(98, 0, 0)
+    hq, hkv, nb = 32, 8, 12
+    kc = wl.normal_bf16(rng, (nb, 256, hkv, D))
+    vc = wl.normal_bf16(rng, (nb, 256, hkv, D))
+    q = wl.normal_bf16(rng, (3, hq, D))
+    bt = np.array([[3, 7, -1, -1], [0, 5, 11, 1000], [2, 9, 4, -1]], np.int32)
+    ctx = np.array([700, 1000, 700], np.int32)
+    o = pkv.attn_decode_paged(to_dev(q, dev), to_dev(kc, dev), to_dev(vc, dev), to_dev(ctx, dev), to_dev(bt, dev))
+    torch.cuda.synchronize()
+    kept = np.array([512, 768, 700], np.int32)          # keys before the unusable block (row 2 is valid)
+    bt_ok = np.where(bt < 0, 0, np.minimum(bt, nb - 1)).astype(np.int32)
+    ref = oracle.attn_decode(q, kc.reshape(-1, hkv, D), vc.reshape(-1, hkv, D), kept, bt_ok, hq, hkv)
+    check_attn(f64(o), ref, "decode with unusable blocks")
