@@ -28,9 +28,9 @@
 //     j/4, dims 4*(j%4) of a 4-key x 16-dim tile and receives its own dim
 //     across the 4 keys.
 //   * Double-buffered LDS (one barrier per tile); the tile after next is
-//     loaded into registers while the current one is computed.  Tiles of 64
-//     keys never straddle a 256-token block, so the paged loader does one
-//     block-table lookup per tile.  Loads are issued on every path (rows past
+//     loaded into registers while the current one is computed.  Tiles (128
+//     keys with 8 waves, 64 with 4) never straddle a 256-token block, so the
+//     paged loader does one block-table lookup per tile.  Loads are issued on every path (rows past
 //     the last key are clamped) so the compiler's wait counts stay exact.
 //   * Softmax: row max on raw scores, scale folded into one FMA ahead of the
 //     hardware exp2; the running max is a lazy reference that moves only when
@@ -47,11 +47,8 @@ namespace pkv {
 namespace {
 typedef __attribute__((address_space(3))) bf16x4* lds_ptr_t;
 constexpr int kRowsPerWave = 32;
-constexpr int kKT = 64;                    // keys per tile
 constexpr int kKPitch = kHeadDim * 2 + 16;  // bytes per K row in LDS (row-major)
 constexpr int kVPitch = kHeadDim * 2 + 64;  // bytes per V row in LDS (row-major, read transposed)
-constexpr int kKTileBytes = kKT * kKPitch;
-constexpr int kVTileBytes = kKT * kVPitch;
 constexpr float kLazyLog2 = 8.0f;           // the lazy reference max moves when a row grows by > 2^8
 }  // namespace
 
@@ -61,8 +58,15 @@ template <int GW, bool PAGED, int NW>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a, int32_t m_blocks, int32_t n_work,
                                                                   int32_t head_groups) {
     constexpr int kThreads = 64 * NW;
+    // Keys per tile: 128 for the 8-wave workgroup (one per CU, LDS for two 74 KB
+    // tile pairs), 64 for 4 waves (two workgroups per CU).  A tile never
+    // straddles a 256-token block.
+    constexpr int kKT = NW == 8 ? 128 : 64;
+    constexpr int kKH = kKT / 32;                       // 32-key blocks per tile
+    constexpr int kKTileBytes = kKT * kKPitch;
+    constexpr int kVTileBytes = kKT * kVPitch;
     constexpr int kLoadRows = kThreads / 16;            // tile rows one sweep of 16-byte pieces covers
-    constexpr int kLoadIters = kKT / kLoadRows;         // sweeps per 64-row tile
+    constexpr int kLoadIters = kKT / kLoadRows;         // sweeps per tile
     constexpr int kPosSub = NW / GW;                    // position sub-blocks per workgroup
     constexpr int kBM = kRowsPerWave * kPosSub;         // query positions per workgroup
     __shared__ __attribute__((aligned(16))) unsigned char k_lds[2 * kKTileBytes];
@@ -120,7 +124,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a,
     const float lazy_raw = kLazyLog2 / a.scale_log2;
 
     // ---- tile loader.  Thread tid moves 16-byte piece tid%16 of rows tid/16 + kLoadRows*i
-    // (i < kLoadIters) of the 64-row K and V tiles.  Row offsets are loop-invariant; every
+    // (i < kLoadIters) of the K and V tiles.  Row offsets are loop-invariant; every
     // load is issued on every path (rows past the last key are clamped onto it), so
     // the compiler's wait counts stay exact.
     const int64_t krs = a.k_row_stride, vrs = a.v_row_stride;
@@ -207,19 +211,19 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a,
           const int j0 = t * kKT;
         bool ok;
         (void)tile_row0(t, ok);
-        // ---- S^T = K Q^T for two 32-key halves
-        // The two key halves are independent accumulation chains; interleaving them
+        // ---- S^T = K Q^T for the tile's 32-key blocks
+        // The key blocks are independent accumulation chains; interleaving them
         // keeps consecutive MFMAs independent so each issues without waiting for the
         // previous result.
-        f32x16 s[2];
+        f32x16 s[kKH];
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
+        for (int kh = 0; kh < kKH; ++kh)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kh][r] = 0.f;
 #pragma unroll
         for (int st = 0; st < 8; ++st)
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
+            for (int kh = 0; kh < kKH; ++kh) {
                 const unsigned char* kr = kb + (32 * kh + (lane & 31)) * kKPitch + 16 * h32;
                 const bf16x8 av = *reinterpret_cast<const bf16x8*>(kr + 32 * st);
                 s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[st], s[kh], 0, 0, 0);
@@ -230,7 +234,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a,
             // key j0 + 4*h32 + c (c a compile-time offset) is visible iff c <= lim
             const int lim = ok ? min(qpos, Lk - 1) - (j0 + 4 * h32) : -1;
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
+            for (int kh = 0; kh < kKH; ++kh)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int c = 32 * kh + 8 * (r >> 2) + (r & 3);
@@ -239,7 +243,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a,
         }
         float tmax = -INFINITY;
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
+        for (int kh = 0; kh < kKH; ++kh)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) tmax = __builtin_fmaxf(__builtin_fmaxf(tmax, s[kh][r]), s[kh][r + 1]);
         {
@@ -263,9 +267,9 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a,
         }
         const float moff = m_run == -INFINITY ? 0.f : -m_run * a.scale_log2;
         float psum = 0.f;
-        uint32_t pk[2][8];
+        uint32_t pk[kKH][8];
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
+        for (int kh = 0; kh < kKH; ++kh)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
                 const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kh][r], a.scale_log2, moff));
@@ -281,7 +285,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a,
         // of a 4-key x 16-dim tile and receives its own dim across the 4 keys.
         const int grp16 = lane >> 4, j16 = lane & 15;
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
+        for (int kh = 0; kh < kKH; ++kh)
 #pragma unroll
             for (int v = 0; v < 2; ++v) {
                 u32x4 bw = {pk[kh][4 * v], pk[kh][4 * v + 1], pk[kh][4 * v + 2], pk[kh][4 * v + 3]};
