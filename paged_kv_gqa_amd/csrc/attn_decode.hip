@@ -9,16 +9,18 @@
 // exp(m_old - m_new).
 //
 // Design (HBM-bound: every K/V byte of the context is read once):
-//   * Split-K: a workgroup owns (sequence b, kv head g, split s) and covers
-//     up to 16 consecutive logical 256-token blocks; the whole GQA group of q
-//     heads is served by one read of K/V.  A one-workgroup kernel first sorts
-//     the split items by size (counting sort), and workgroups take them largest
-//     first: with contexts of very different lengths the last workgroups to
-//     start are the smallest, so the tail stays short.
-//   * Inside the workgroup each of the 4 waves streams its own 16-key slice
-//     of every 64-key quarter block and keeps its own online-softmax state, so
-//     the main loop has no workgroup barrier at all.  Loads run one chunk
-//     ahead in a register ring.
+//   * Split-K: a workgroup owns (sequence b, a group of 4 kv heads, split s)
+//     and covers up to 8 consecutive logical 256-token blocks.  Each of its 4
+//     waves owns one kv head and streams the whole split for it, so the waves
+//     read adjacent 256-byte pieces of every 2 KiB cache row (1 KiB per key
+//     and workgroup), each wave keeps its own online-softmax state and there
+//     is no barrier and no cross-wave merge.  The whole GQA group of q heads
+//     of a kv head is served by one read of its K/V.
+//   * A one-workgroup kernel first sorts the split items by size (counting
+//     sort), and workgroups take them largest first: with contexts of very
+//     different lengths the last workgroups to start are the smallest, so the
+//     tail stays short.
+//   * Loads run one 16-key chunk ahead in a register ring.
 //   * Both products on MFMA.  Scores: v_mfma_f32_16x16x32_bf16 with A = 16 keys
 //     x 32 dims straight from global memory and B = the group's q vectors
 //     (columns >= G are zero); a lane then holds 4 keys of one head column.
@@ -33,9 +35,9 @@
 //   * Keys at or past the context length and keys of a block id outside the
 //     pool are masked before the exponential and their V rows replaced by
 //     zeros, so nothing outside the context can reach the output.
-//   * The 4 waves merge once at the end; the split's (m, l, O) go to a
-//     caller-owned fp32 workspace and a second kernel merges the splits of
-//     each (b, h) in split order (deterministic).
+//   * Each wave writes its split's (m, l, O) to a caller-owned fp32 workspace
+//     and a second kernel merges the splits of each (b, h) in split order
+//     (deterministic).
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -43,11 +45,11 @@ namespace pkv {
 
 namespace {
 constexpr int kDecThreads = 256;
-// Tuning (measured on MI355X, Qwen3-8B decode workload): splits of up to 16
+// Tuning (measured on MI355X, Qwen3-8B decode workload): splits of up to 8
 // blocks, a ring of 2 chunks of 16 keys per wave, 2 waves per SIMD.  Longer
 // splits amortise each workgroup's pipeline fill; deeper rings did not pay.
 #ifndef PKV_DECODE_SPLIT
-#define PKV_DECODE_SPLIT 16
+#define PKV_DECODE_SPLIT 8
 #endif
 #ifndef PKV_DECODE_DEPTH
 #define PKV_DECODE_DEPTH 2
@@ -60,7 +62,6 @@ constexpr int kTargetItems = 4096;
 constexpr float kLazyMax = 8.0f;   // log2 headroom of the lazy reference max
 constexpr int kDepth = PKV_DECODE_DEPTH;   // register ring: chunks in flight + the one computed
 constexpr int kCK = 16;                    // keys per wave per chunk (one 16-key MFMA tile)
-constexpr int kRounds = kBlockSize / (4 * kCK);  // chunks per 256-token block per wave
 constexpr int kOcc = PKV_DECODE_OCC;       // waves per SIMD the register budget is sized for
 
 struct Workspace {
@@ -91,7 +92,7 @@ struct Chunk {
 int decode_split_blocks(int32_t num_seqs, int32_t hkv, int32_t max_blocks) {
     int sb = kMaxSplitBlocks;
     while (sb > 1) {
-        const int64_t items = (int64_t)num_seqs * hkv * ((max_blocks + sb - 1) / sb);
+        const int64_t items = (int64_t)num_seqs * ((hkv + 3) / 4) * ((max_blocks + sb - 1) / sb);
         if (items >= kTargetItems) break;
         sb >>= 1;
     }
@@ -117,8 +118,11 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
     // Dispatch order: split items by decreasing size (full splits first), so the
     // smallest pieces of work come last and the tail stays short.
     const int item = work[(int64_t)blockIdx.z * gridDim.y + blockIdx.y];
-    const int g = blockIdx.x, b = item / max_splits, s = item - b * max_splits;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // Each wave owns one kv head of a group of 4 (the 4 waves read adjacent 256-byte
+    // pieces of every 2 KiB cache row) and streams the whole split for it.
+    const int g = 4 * blockIdx.x + wave, b = item / max_splits, s = item - b * max_splits;
+    if (g >= hkv) return;
 
     int ctx = context_lens[b];
     const int cap = max_blocks * kBlockSize;
@@ -127,12 +131,10 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
     const int blk0 = s * split_blocks;
     if (blk0 >= nblk) return;
     const int nb = min(split_blocks, nblk - blk0);   // blocks of this split
-    const int nchunks = nb * kRounds;                // chunks of 64 keys; this wave owns 16 of each
+    const int nchunks = nb * (kBlockSize / kCK);     // 16-key chunks of the split, all for this wave
 
     constexpr int kVPitch = kHeadDim * 2 + 32;       // bytes per V row in LDS (conflict-free transposed reads)
     __shared__ __attribute__((aligned(16))) unsigned char s_v[4][kCK * kVPitch];   // per-wave V tile
-    __shared__ float s_m[4][G], s_l[4][G];           // per-wave final max / sum
-    __shared__ float s_o[4][G][kHeadDim];            // per-wave final numerators
 
     const int64_t row = (int64_t)hkv * kHeadDim;    // elements between consecutive cache rows
 
@@ -157,9 +159,10 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
         }
     }
 
-    // Chunk j covers keys 16*(4*(j%kRounds) + wave) .. +15 of block blk0 + j/kRounds.
-    auto block_of = [&](int j) { return __builtin_amdgcn_readlane(my_blk, j / kRounds); };
-    auto chunk_row0 = [&](int j) { return kCK * (4 * (j % kRounds) + wave); };
+    // Chunk j covers keys 16*(j%16) .. +15 of block blk0 + j/16.
+    constexpr int kCPB = kBlockSize / kCK;           // chunks per block
+    auto block_of = [&](int j) { return __builtin_amdgcn_readlane(my_blk, j / kCPB); };
+    auto chunk_row0 = [&](int j) { return kCK * (j % kCPB); };
     auto load = [&](Chunk& c, int j) {
         const int id = block_of(j);
         const int64_t phys = id < 0 ? 0 : id;
@@ -184,7 +187,7 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
     typedef __attribute__((address_space(3))) bf16x4* lds4_t;
 
     auto compute = [&](const Chunk& c, int j) {
-        const int key0 = (blk0 + j / kRounds) * kBlockSize + chunk_row0(j);
+        const int key0 = (blk0 + j / kCPB) * kBlockSize + chunk_row0(j);
         const int id = block_of(j);
         // ---- V rows into this wave's LDS tile; keys outside the context become zeros
 #pragma unroll
@@ -252,40 +255,19 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
         }
     }
 
-    // ---- merge the 4 waves: per head (m, l, O)
+    // ---- this wave's (m, l, O) for its G heads go straight to the workspace
     float lsum = l_run;
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
-    if (lane < G) {
-        s_m[wave][lane] = m_ref;
-        s_l[wave][lane] = lsum;
-    }
     if (col < G) {
+        const int64_t bh = (int64_t)b * hq + (int64_t)g * G + col;
+        float* po = part_o + (bh * max_splits + s) * kHeadDim;
 #pragma unroll
-        for (int d = 0; d < 8; ++d)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s_o[wave][col][16 * d + 4 * grp + r] = acc[d][r];
-    }
-    __syncthreads();
-    const int64_t bh0 = (int64_t)b * hq + (int64_t)g * G;
-    for (int x = tid; x < G * kHeadDim; x += kDecThreads) {
-        const int h = x / kHeadDim, d = x % kHeadDim;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][h]);
-        const float ref = M == -INFINITY ? 0.f : M;
-        float o = 0.f, L = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float f = exp2f(s_m[w][h] - ref);
-            o = fmaf(s_o[w][h][d], f, o);
-            L = fmaf(s_l[w][h], f, L);
-        }
-        part_o[((bh0 + h) * max_splits + s) * kHeadDim + d] = o;
-        if (d == 0) {
-            float* ml = part_ml + ((bh0 + h) * max_splits + s) * 2;
-            ml[0] = M;
-            ml[1] = L;
+        for (int d = 0; d < 8; ++d) *reinterpret_cast<f32x4*>(po + 16 * d + 4 * grp) = acc[d];
+        if (grp == 0) {
+            float* ml = part_ml + (bh * max_splits + s) * 2;
+            ml[0] = m_ref;
+            ml[1] = lsum;
         }
     }
 }
@@ -384,7 +366,7 @@ hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t stream) {
     Workspace w = carve(a.workspace, a.num_seqs, a.hq, ms);
     hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(1024), 0, stream, a.context_lens, a.max_blocks, a.num_seqs,
                        sb, ms, w.work);
-    dim3 grid(a.hkv, a.num_seqs, ms);
+    dim3 grid((a.hkv + 3) / 4, a.num_seqs, ms);
 #define PKV_DECODE_CASE(GG)                                                                                       \
     case GG:                                                                                                      \
         hipLaunchKernelGGL(decode_split_kernel<GG>, grid, dim3(kDecThreads), 0, stream, (const uint16_t*)a.q,     \
