@@ -58,7 +58,10 @@ constexpr int kDecThreads = 256;
 #define PKV_DECODE_OCC 2
 #endif
 constexpr int kMaxSplitBlocks = PKV_DECODE_SPLIT;   // blocks per split-K work item (at most)
-constexpr int kTargetItems = 4096;
+#ifndef PKV_DECODE_TARGET
+#define PKV_DECODE_TARGET 2048
+#endif
+constexpr int kTargetItems = PKV_DECODE_TARGET;
 constexpr float kLazyMax = 8.0f;   // log2 headroom of the lazy reference max
 constexpr int kDepth = PKV_DECODE_DEPTH;   // register ring: chunks in flight + the one computed
 constexpr int kCK = 16;                    // keys per wave per chunk (one 16-key MFMA tile)
