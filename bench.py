@@ -194,6 +194,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in events])) for j, n in enumerate(names)}
+    spread = {n: (float(np.median([e[j].elapsed_time(e[j + 1]) for e in events])),
+                  float(np.min([e[j].elapsed_time(e[j + 1]) for e in events]))) for j, n in enumerate(names)}
     ms_step = wall * 1e3 / args.steps
 
     # the unfused first steps, timed after the step loop (not part of ms_per_step)
@@ -219,9 +221,11 @@ def main():
         return nbytes / (ms * 1e-3) / 1e9
 
     kernels = {
-        "attn_decode_paged": {"ms": per["decode"], "GB/s": dec_gbs, "bytes": dec_bytes,
+        "attn_decode_paged": {"ms": per["decode"], "ms_median": spread["decode"][0], "ms_min": spread["decode"][1],
+                              "GB/s": dec_gbs, "bytes": dec_bytes,
                               "logical_bytes": wd.algorithmic_bytes(unique=False)},
-        "attn_prefill_varlen": {"ms": per["prefill"], "TFLOP/s": pre_tflops, "flop": wp.flops},
+        "attn_prefill_varlen": {"ms": per["prefill"], "ms_median": spread["prefill"][0],
+                                "ms_min": spread["prefill"][1], "TFLOP/s": pre_tflops, "flop": wp.flops},
         "qk_norm_rope_store_prefill": {"ms": per["norm_rope_store_p"],
                                        "GB/s": gbs(fused_bytes, per["norm_rope_store_p"]), "bytes": fused_bytes},
         "qk_norm_rope_store_decode": {"ms": per["norm_rope_store_d"]},
@@ -235,6 +239,8 @@ def main():
     log(json.dumps(kernels))
 
     ops = sublayer_ops(pkv, torch, dev, to_dev, args, log)
+    norm_small = norm_rope_small(pkv, torch, dev, table, args, log)
+    copy_ref = copy_reference(torch, dev, log)
 
     ladder = decode_graph_ladder(pkv, torch, s8, table, qkv_d, kc_d, vc_d, pos_d, slot_d, cl_d, bt_d, gq_d, gk_d,
                                  args, log)
@@ -266,7 +272,8 @@ def main():
         "prefill": {"value": round(pre_tflops, 2), "unit": "TFLOP/s", "ms": round(per["prefill"], 4)},
         "roofline": {"bound": "hbm", "kernel": "attn_decode_paged", "achieved": round(dec_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic("attn_decode_paged_qwen3_8b_hbm_traffic.md", "attn_decode.hip")},
+                     "traffic": recorded_traffic("attn_decode_paged_qwen3_8b_hbm_traffic.md", "attn_decode.hip"),
+                     "measured_copy_GB/s": copy_ref["copy_GB/s"]},
         "roofline_prefill": {"bound": "mfma", "kernel": "attn_prefill_varlen", "achieved": round(pre_tflops, 2),
                              "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
@@ -276,10 +283,74 @@ def main():
                     for k, v in kernels.items()},
         "cpu_baseline": cpu,
         "sublayer_ops": ops,
+        "qk_norm_rope_small": norm_small,
         "decode_graph": ladder,
         "cpu_baseline_prefill": cpu_pre,
     }
     print(json.dumps(out), flush=True)
+
+
+def copy_reference(torch, dev, log):
+    """What a plain streaming kernel reaches on this device, for context beside the
+    8 TB/s peak: a device-to-device copy of 1 GiB, bytes read + written per second,
+    best of five.  (The decode only reads; a copy mixes reads and writes, which
+    streams more slowly, so the decode's rate can exceed it.)"""
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+
+    def best(fn):
+        fn()
+        times = []
+        for _ in range(5):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            fn()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            times.append(ev[0].elapsed_time(ev[1]))
+        return min(times)
+
+    copy_ms = best(lambda: dst.copy_(src))
+    out = {"copy_GB/s": round(2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9, 1)}
+    log(f"streaming reference: {out}")
+    del src, dst
+    return out
+
+
+def norm_rope_small(pkv, torch, dev, table, args, log):
+    """QK-Norm + RoPE (the unfused pass) at the Qwen3-0.6B head counts (16 q / 8 kv) on
+    the token counts of the small correctness workload (337) and of the 0.6B varlen
+    prefill (its eight lengths): secondary HBM-bound numbers."""
+    import workloads as wl
+    s6 = wl.QWEN3_0_6B
+    D = 128
+    out = {}
+    for label, T in (("tiny_337", 337), ("varlen_prefill", int(wl.varlen_prefill(args.seed).lengths.sum()))):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed + T)
+        qkv = torch.randn((T, s6.qkv_width), generator=gen, device=dev).to(torch.bfloat16)
+        q0, k0, v0 = wl.qkv_views(s6)
+        q = qkv[:, q0:k0].view(T, s6.num_q_heads, D)
+        k = qkv[:, k0:v0].view(T, s6.num_kv_heads, D)
+        pos = torch.arange(T, dtype=torch.int64, device=dev) % 4096
+        g = torch.ones(D, dtype=torch.bfloat16, device=dev)
+        qo = torch.empty((T, s6.num_q_heads, D), dtype=torch.bfloat16, device=dev)
+        ko = torch.empty((T, s6.num_kv_heads, D), dtype=torch.bfloat16, device=dev)
+        fn = lambda: pkv.qk_norm_rope(q, k, pos, g, g, table, s6.eps, q_out=qo, k_out=ko)
+        for _ in range(args.warmup):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(torch.cuda.current_stream())
+        for _ in range(args.steps):
+            fn()
+        ev[1].record(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / args.steps
+        nbytes = T * ((s6.num_q_heads + s6.num_kv_heads) * D * 2 * 2 + 8 + 512)
+        out[label] = {"tokens": T, "ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 2), "bytes": nbytes}
+    log(f"qk_norm_rope at 0.6B shapes: {json.dumps(out)}")
+    return out
 
 
 def sublayer_ops(pkv, torch, dev, to_dev, args, log):
