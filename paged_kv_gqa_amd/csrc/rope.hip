@@ -9,11 +9,13 @@
 // max_position rows looked up by position).
 //
 // Design: the two elementwise steps the pages compile separately are fused
-// into one pass.  Each (token, head) vector of 128 bf16 is owned by 16 lanes,
-// 8 elements (one 16-byte load) per lane.  The sum of squares is a 16-lane
-// butterfly; the rotation partner of elements [8s, 8s+8) lives in lane s ^ 8,
-// fetched with a cross-lane shuffle.  Math is fp32 throughout and the result
-// is rounded to bf16 once.
+// into one pass.  A wave owns one token; each (token, head) vector of 128 bf16
+// is owned by one 16-lane group, 8 elements (one 16-byte load) per lane, and
+// the four groups of the wave walk the token's heads.  The token's cos/sin row
+// and the norm weights are loaded once per wave, not once per head.  The sum
+// of squares is a 16-lane butterfly; the rotation partner of elements
+// [8s, 8s+8) lives in lane s ^ 8, fetched with a cross-lane shuffle.  Math is
+// fp32 throughout and the result is rounded to bf16 once.
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -50,18 +52,17 @@ hipError_t launch_rope_cache_build(float* table, int32_t max_pos, int32_t rot_di
 }
 
 // QK-Norm + RoPE of one 128-element head vector held by a 16-lane group, 8
-// elements per lane (x = this lane's 16-byte chunk, may be zero for dead
-// groups).  All 16 lanes of the group must call it together: the sum of
-// squares and the rotation partner cross lanes.  Returns this lane's 8 output
-// elements packed as bf16 (one RNE rounding of the fp32 result).
-__device__ __forceinline__ u32x4 norm_rope_chunk(u32x4 xo, const uint16_t* __restrict__ g, float eps,
-                                                 const float* __restrict__ table_row, int sub) {
+// elements per lane (xo = this lane's 16-byte chunk, zero for dead groups).
+// go / gp are this lane's and its rotation partner's 8 weights, cv / sv the
+// cos and sin of this lane's 8 frequencies.  All 16 lanes of the group must
+// call it together: the sum of squares and the rotation partner cross lanes.
+// Returns this lane's 8 outputs packed as bf16 (one RNE rounding of the fp32
+// result).
+__device__ __forceinline__ u32x4 norm_rope_apply(u32x4 xo, u32x4 go, u32x4 gp, float eps, const float* cv,
+                                                 const float* sv, int sub) {
     u32x4 xp;
 #pragma unroll
     for (int w = 0; w < 4; ++w) xp[w] = __shfl_xor(xo[w], 8, 16);
-    const u32x4 go = ldg128(g + sub * 8);
-    const u32x4 gp = ldg128(g + (sub ^ 8) * 8);
-
     float xa[8], xb[8];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -76,14 +77,6 @@ __device__ __forceinline__ u32x4 norm_rope_chunk(u32x4 xo, const uint16_t* __res
 #pragma unroll
     for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 16);
     const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps);
-
-    const float* cs = table_row + (sub & 7) * 8;
-    const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs);
-    const f32x4 c1 = *reinterpret_cast<const f32x4*>(cs + 4);
-    const f32x4 s0 = *reinterpret_cast<const f32x4*>(cs + 64);
-    const f32x4 s1 = *reinterpret_cast<const f32x4*>(cs + 68);
-    const float cv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-    const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
     // Lanes 0..7 hold x1 (first half): y1 = x1 c - x2 s.  Lanes 8..15 hold x2: y2 = x2 c + x1 s.
     const float sgn = sub < 8 ? -1.0f : 1.0f;
     u32x4 res;
@@ -104,45 +97,83 @@ __device__ __forceinline__ u32x4 norm_rope_chunk(u32x4 xo, const uint16_t* __res
     return res;
 }
 
-__device__ __forceinline__ const float* rope_row(const float* table, const int64_t* positions, int64_t t, bool live,
+// One token's table row, clamped position.
+__device__ __forceinline__ const float* rope_row(const float* table, const int64_t* positions, int64_t t,
                                                  int32_t max_pos) {
-    int64_t pos = live ? positions[t] : 0;
+    int64_t pos = positions[t];
     pos = pos < 0 ? 0 : (pos >= max_pos ? (int64_t)max_pos - 1 : pos);
     return table + pos * kHeadDim;
 }
 
-// 16 lanes per (token, head) item; 16 items per 256-thread block.
+__device__ __forceinline__ void load_cos_sin(const float* __restrict__ row, int sub, float* cv, float* sv) {
+    const float* cs = row + (sub & 7) * 8;
+    const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs);
+    const f32x4 c1 = *reinterpret_cast<const f32x4*>(cs + 4);
+    const f32x4 s0 = *reinterpret_cast<const f32x4*>(cs + 64);
+    const f32x4 s1 = *reinterpret_cast<const f32x4*>(cs + 68);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        cv[i] = c0[i];
+        cv[4 + i] = c1[i];
+        sv[i] = s0[i];
+        sv[4 + i] = s1[i];
+    }
+}
+
+// A wave owns one token; its four 16-lane groups take that token's heads in
+// turn (head g, g+4, ...), kChunk heads per group loaded before any is stored,
+// so several loads are in flight even when the outputs alias the inputs.  The
+// table row and the weights are loaded once per token.
+constexpr int kChunk = 4;
+
+template <typename LoadF, typename StoreF>
+__device__ __forceinline__ void norm_rope_heads(int n_heads, int grp, int sub, u32x4 go, u32x4 gp, float eps,
+                                                const float* cv, const float* sv, LoadF load, StoreF store) {
+    for (int h0 = 0; h0 < n_heads; h0 += 4 * kChunk) {
+        u32x4 x[kChunk];
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c) {
+            const int h = h0 + 4 * c + grp;
+            x[c] = h < n_heads ? load(h) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c) {
+            const int h = h0 + 4 * c + grp;
+            if (h0 + 4 * c >= n_heads) break;          // no group of the wave has this head (uniform)
+            const u32x4 res = norm_rope_apply(x[c], go, gp, eps, cv, sv, sub);
+            if (h < n_heads) store(h, res);
+        }
+    }
+}
+
+// 4 tokens per 256-thread block, one per wave.
 __global__ void __launch_bounds__(256) qk_norm_rope_kernel(
     const uint16_t* q, int64_t q_row_stride, const uint16_t* k, int64_t k_row_stride,  // may alias the outputs
     uint16_t* q_out, uint16_t* k_out, const int64_t* __restrict__ positions, int32_t n_tokens, int32_t hq,
     int32_t hkv, const uint16_t* __restrict__ gq, const uint16_t* __restrict__ gk, float eps,
     const float* __restrict__ table, int32_t max_pos) {
-    const int heads = hq + hkv;
-    const int64_t item = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int sub = threadIdx.x & 15;
-    const int64_t n_items = (int64_t)n_tokens * heads;
-    // Items past the end still take part in the shuffles (all 16 lanes of a
-    // group share the same item, so a whole group is either in or out).
-    const bool live = item < n_items;
-    const int64_t it = live ? item : 0;
-    const int64_t t = it / heads;
-    const int h = (int)(it - t * heads);
-    const bool is_q = h < hq;
-    const uint16_t* src = is_q ? q + t * q_row_stride + (int64_t)h * kHeadDim
-                               : k + t * k_row_stride + (int64_t)(h - hq) * kHeadDim;
-    uint16_t* dst = is_q ? q_out + (t * hq + h) * kHeadDim : k_out + (t * hkv + (h - hq)) * kHeadDim;
-
-    const u32x4 xo = live ? ldg128(src + sub * 8) : u32x4{0u, 0u, 0u, 0u};
-    const u32x4 res = norm_rope_chunk(xo, is_q ? gq : gk, eps, rope_row(table, positions, t, live, max_pos), sub);
-    if (live) stg128(dst + sub * 8, res);
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= n_tokens) return;                       // the whole wave leaves together
+    const int lane = threadIdx.x & 63, grp = lane >> 4, sub = lane & 15;
+    float cv[8], sv[8];
+    load_cos_sin(rope_row(table, positions, t, max_pos), sub, cv, sv);
+    const uint16_t* qt = q + t * q_row_stride + sub * 8;
+    uint16_t* qo = q_out + t * hq * kHeadDim + sub * 8;
+    norm_rope_heads(hq, grp, sub, ldg128(gq + sub * 8), ldg128(gq + (sub ^ 8) * 8), eps, cv, sv,
+                    [&](int h) { return ldg128(qt + (int64_t)h * kHeadDim); },
+                    [&](int h, u32x4 r) { stg128(qo + (int64_t)h * kHeadDim, r); });
+    const uint16_t* kt = k + t * k_row_stride + sub * 8;
+    uint16_t* ko = k_out + t * hkv * kHeadDim + sub * 8;
+    norm_rope_heads(hkv, grp, sub, ldg128(gk + sub * 8), ldg128(gk + (sub ^ 8) * 8), eps, cv, sv,
+                    [&](int h) { return ldg128(kt + (int64_t)h * kHeadDim); },
+                    [&](int h, u32x4 r) { stg128(ko + (int64_t)h * kHeadDim, r); });
 }
 
-// QK-Norm + RoPE fused with the cache scatter.  Per token the items are the
-// Hq query heads, the Hkv key heads and the Hkv value heads (16 lanes each).
-// Query heads go to q_out; rotated key heads go straight to k_cache row
+// QK-Norm + RoPE fused with the cache scatter, one token per wave.  Query
+// heads go to q_out; rotated key heads go straight to k_cache row
 // slot_mapping[t] (and to k_out when it is given); value heads are copied to
-// v_cache row slot_mapping[t].  A slot outside [0, num_slots) (the padding
-// id -1 included) writes no cache row.
+// v_cache row slot_mapping[t].  A slot outside [0, num_slots) (the padding id
+// -1 included) writes no cache row.
 __global__ void __launch_bounds__(256) qk_norm_rope_store_kernel(
     const uint16_t* q, int64_t q_row_stride, const uint16_t* k, int64_t k_row_stride,
     const uint16_t* __restrict__ v, int64_t v_row_stride, uint16_t* q_out, uint16_t* k_out,
@@ -150,46 +181,55 @@ __global__ void __launch_bounds__(256) qk_norm_rope_store_kernel(
     const int32_t* __restrict__ slot_mapping, const int64_t* __restrict__ positions, int32_t n_tokens, int32_t hq,
     int32_t hkv, const uint16_t* __restrict__ gq, const uint16_t* __restrict__ gk, float eps,
     const float* __restrict__ table, int32_t max_pos) {
-    const int heads = hq + 2 * hkv;
-    const int64_t item = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int sub = threadIdx.x & 15;
-    const bool live = item < (int64_t)n_tokens * heads;
-    const int64_t it = live ? item : 0;
-    const int64_t t = it / heads;
-    const int h = (int)(it - t * heads);
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= n_tokens) return;
+    const int lane = threadIdx.x & 63, grp = lane >> 4, sub = lane & 15;
     const int64_t D = (int64_t)hkv * kHeadDim;
-    const int64_t slot = live ? (int64_t)slot_mapping[t] : -1;
+    const int64_t slot = (int64_t)slot_mapping[t];
     const bool to_cache = slot >= 0 && slot < num_slots;
+    uint16_t* kc = to_cache ? k_cache + slot * D + sub * 8 : nullptr;
 
-    if (h >= hq + hkv) {  // value head: plain copy into the cache (the whole group takes this branch)
-        const int hv = h - hq - hkv;
-        if (to_cache)
-            stg128(v_cache + slot * D + (int64_t)hv * kHeadDim + sub * 8,
-                   ldg128(v + t * v_row_stride + (int64_t)hv * kHeadDim + sub * 8));
-        return;
+    // value heads: plain copies into the cache row
+    if (to_cache) {
+        const uint16_t* vt = v + t * v_row_stride + sub * 8;
+        uint16_t* vc = v_cache + slot * D + sub * 8;
+        for (int h0 = 0; h0 < hkv; h0 += 4 * kChunk) {
+            u32x4 x[kChunk];
+#pragma unroll
+            for (int c = 0; c < kChunk; ++c) {
+                const int h = h0 + 4 * c + grp;
+                if (h < hkv) x[c] = ldg128(vt + (int64_t)h * kHeadDim);
+            }
+#pragma unroll
+            for (int c = 0; c < kChunk; ++c) {
+                const int h = h0 + 4 * c + grp;
+                if (h < hkv) stg128(vc + (int64_t)h * kHeadDim, x[c]);
+            }
+        }
     }
-    const bool is_q = h < hq;
-    const uint16_t* src = is_q ? q + t * q_row_stride + (int64_t)h * kHeadDim
-                               : k + t * k_row_stride + (int64_t)(h - hq) * kHeadDim;
-    const u32x4 xo = live ? ldg128(src + sub * 8) : u32x4{0u, 0u, 0u, 0u};
-    const u32x4 res = norm_rope_chunk(xo, is_q ? gq : gk, eps, rope_row(table, positions, t, live, max_pos), sub);
-    if (!live) return;
-    if (is_q) {
-        stg128(q_out + (t * hq + h) * kHeadDim + sub * 8, res);
-    } else {
-        const int hk = h - hq;
-        if (k_out) stg128(k_out + (t * hkv + hk) * kHeadDim + sub * 8, res);
-        if (to_cache) stg128(k_cache + slot * D + (int64_t)hk * kHeadDim + sub * 8, res);
-    }
+    float cv[8], sv[8];
+    load_cos_sin(rope_row(table, positions, t, max_pos), sub, cv, sv);
+    const uint16_t* qt = q + t * q_row_stride + sub * 8;
+    uint16_t* qo = q_out + t * hq * kHeadDim + sub * 8;
+    norm_rope_heads(hq, grp, sub, ldg128(gq + sub * 8), ldg128(gq + (sub ^ 8) * 8), eps, cv, sv,
+                    [&](int h) { return ldg128(qt + (int64_t)h * kHeadDim); },
+                    [&](int h, u32x4 r) { stg128(qo + (int64_t)h * kHeadDim, r); });
+    const uint16_t* kt = k + t * k_row_stride + sub * 8;
+    uint16_t* ko = k_out ? k_out + t * hkv * kHeadDim + sub * 8 : nullptr;
+    norm_rope_heads(hkv, grp, sub, ldg128(gk + sub * 8), ldg128(gk + (sub ^ 8) * 8), eps, cv, sv,
+                    [&](int h) { return ldg128(kt + (int64_t)h * kHeadDim); },
+                    [&](int h, u32x4 r) {
+                        if (ko) stg128(ko + (int64_t)h * kHeadDim, r);
+                        if (kc) stg128(kc + (int64_t)h * kHeadDim, r);
+                    });
 }
 
 hipError_t launch_qk_norm_rope(const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride,
                                void* q_out, void* k_out, const int64_t* positions, int32_t n_tokens,
                                int32_t hq, int32_t hkv, const void* gq, const void* gk, float eps,
                                const float* table, int32_t max_pos, hipStream_t stream) {
-    const int64_t items = (int64_t)n_tokens * (hq + hkv);
-    if (items == 0) return hipSuccess;
-    const int64_t blocks = (items + 15) / 16;
+    if (n_tokens == 0) return hipSuccess;
+    const int64_t blocks = ((int64_t)n_tokens + 3) / 4;
     hipLaunchKernelGGL(qk_norm_rope_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        (const uint16_t*)q, q_row_stride, (const uint16_t*)k, k_row_stride, (uint16_t*)q_out,
                        (uint16_t*)k_out, positions, n_tokens, hq, hkv, (const uint16_t*)gq, (const uint16_t*)gk,
@@ -203,9 +243,8 @@ hipError_t launch_qk_norm_rope_store(const void* q, int64_t q_row_stride, const 
                                      const int64_t* positions, int32_t n_tokens, int32_t hq, int32_t hkv,
                                      const void* gq, const void* gk, float eps, const float* table, int32_t max_pos,
                                      hipStream_t stream) {
-    const int64_t items = (int64_t)n_tokens * (hq + 2 * hkv);
-    if (items == 0) return hipSuccess;
-    const int64_t blocks = (items + 15) / 16;
+    if (n_tokens == 0) return hipSuccess;
+    const int64_t blocks = ((int64_t)n_tokens + 3) / 4;
     hipLaunchKernelGGL(qk_norm_rope_store_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const uint16_t*)q,
                        q_row_stride, (const uint16_t*)k, k_row_stride, (const uint16_t*)v, v_row_stride,
                        (uint16_t*)q_out, (uint16_t*)k_out, (uint16_t*)k_cache, (uint16_t*)v_cache, num_slots,
