@@ -402,7 +402,8 @@ class PrefixPrefill:
 
     @property
     def store_bytes(self) -> int:
-        return self.num_q_tokens * (2 * 2 * self.shape.kv_size + 4)
+        # per token: the K and V rows read and written (2 x 2 x kv_size bf16) + the 4-byte slot id
+        return self.num_q_tokens * (2 * 2 * 2 * self.shape.kv_size + 4)
 
 
 def prefix_prefill_8b(seed: int = 0, num_seqs: int = 16, prefix_len: int = 2048, total_len: int = 4096,
