@@ -105,23 +105,23 @@ __global__ void __launch_bounds__(256) add_rms_norm_kernel(const uint16_t* x, co
 __global__ void __launch_bounds__(256) silu_and_mul_kernel(const uint16_t* __restrict__ x, int64_t x_row_stride,
                                                            uint16_t* __restrict__ out, int64_t out_row_stride,
                                                            int32_t n_tokens, int32_t inter) {
-    const int cpr = inter >> 3;
-    const int64_t total = (int64_t)n_tokens * cpr;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t t = e / cpr;
-        const int c = (int)(e - t * cpr);
+    const int cpr = inter >> 3;   // 8-element chunks per row
+    for (int64_t t = blockIdx.x; t < n_tokens; t += gridDim.x) {
         const uint16_t* row = x + t * x_row_stride;
-        const u32x4 gv = ldg128(row + 8 * c);
-        const u32x4 uv = ldg128(row + inter + 8 * c);
-        u32x4 o;
+        uint16_t* orow = out + t * out_row_stride;
+        for (int c = threadIdx.x; c < cpr; c += blockDim.x) {
+            const u32x4 gv = ldg128(row + 8 * c);
+            const u32x4 uv = ldg128(row + inter + 8 * c);
+            u32x4 o;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float g0 = bf16lo(gv[w]), g1 = bf16hi(gv[w]);
-            const float a0 = g0 / (1.0f + __expf(-g0)) * bf16lo(uv[w]);
-            const float a1 = g1 / (1.0f + __expf(-g1)) * bf16hi(uv[w]);
-            o[w] = pack_bf16x2(a0, a1);
+            for (int w = 0; w < 4; ++w) {
+                const float g0 = bf16lo(gv[w]), g1 = bf16hi(gv[w]);
+                const float a0 = g0 / (1.0f + __expf(-g0)) * bf16lo(uv[w]);
+                const float a1 = g1 / (1.0f + __expf(-g1)) * bf16hi(uv[w]);
+                o[w] = pack_bf16x2(a0, a1);
+            }
+            stg128(orow + 8 * c, o);
         }
-        stg128(out + t * out_row_stride + 8 * c, o);
     }
 }
 
@@ -308,10 +308,9 @@ hipError_t launch_add_rms_norm(const void* x, const void* residual, const void* 
 
 hipError_t launch_silu_and_mul(const void* x, int64_t x_row_stride, void* out, int64_t out_row_stride,
                                int32_t n_tokens, int32_t inter, hipStream_t stream) {
-    const int64_t total = (int64_t)n_tokens * (inter / 8);
-    if (total == 0) return hipSuccess;
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
+    if ((int64_t)n_tokens * (inter / 8) == 0) return hipSuccess;
+    // one workgroup per row at a time, rows strided over the grid
+    const int64_t blocks = n_tokens < 16384 ? n_tokens : 16384;
     hipLaunchKernelGGL(silu_and_mul_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const uint16_t*)x,
                        x_row_stride, (uint16_t*)out, out_row_stride, n_tokens, inter);
     return hipGetLastError();
