@@ -9,10 +9,11 @@
 // max_position rows looked up by position).
 //
 // Design: the two elementwise steps the pages compile separately are fused
-// into one pass.  A wave owns one token; each (token, head) vector of 128 bf16
-// is owned by one 16-lane group, 8 elements (one 16-byte load) per lane, and
-// the four groups of the wave walk the token's heads.  The token's cos/sin row
-// and the norm weights are loaded once per wave, not once per head.  The sum
+// into one pass.  A wave owns one token (or, for short batches, a chunk of its
+// heads); each (token, head) vector of 128 bf16 is owned by one 16-lane group,
+// 8 elements (one 16-byte load) per lane, and the four groups of the wave walk
+// the heads.  The cos/sin row and the norm weights are loaded once per wave,
+// not once per head.  The sum
 // of squares is a 16-lane butterfly; the rotation partner of elements
 // [8s, 8s+8) lives in lane s ^ 8, fetched with a cross-lane shuffle.  Math is
 // fp32 throughout and the result is rounded to bf16 once.
@@ -120,69 +121,81 @@ __device__ __forceinline__ void load_cos_sin(const float* __restrict__ row, int 
     }
 }
 
-// A wave owns one token; its four 16-lane groups take that token's heads in
-// turn (head g, g+4, ...), kChunk heads per group loaded before any is stored,
-// so several loads are in flight even when the outputs alias the inputs.  The
-// table row and the weights are loaded once per token.
+// A wave owns one token, or for short batches one chunk of a token's heads
+// (hpw heads, a multiple of 4; the heads are numbered q, then k, then v).  Its
+// four 16-lane groups take the chunk's heads in turn (head lo+g, lo+g+4, ...),
+// kChunk heads per group loaded before any is stored, so several loads are in
+// flight even when the outputs alias the inputs.  The table row and the
+// weights are loaded once per wave.
 constexpr int kChunk = 4;
 
 template <typename LoadF, typename StoreF>
-__device__ __forceinline__ void norm_rope_heads(int n_heads, int grp, int sub, u32x4 go, u32x4 gp, float eps,
+__device__ __forceinline__ void norm_rope_heads(int lo, int hi, int grp, int sub, u32x4 go, u32x4 gp, float eps,
                                                 const float* cv, const float* sv, LoadF load, StoreF store) {
-    for (int h0 = 0; h0 < n_heads; h0 += 4 * kChunk) {
+    for (int h0 = lo; h0 < hi; h0 += 4 * kChunk) {
         u32x4 x[kChunk];
 #pragma unroll
         for (int c = 0; c < kChunk; ++c) {
             const int h = h0 + 4 * c + grp;
-            x[c] = h < n_heads ? load(h) : u32x4{0u, 0u, 0u, 0u};
+            x[c] = h < hi ? load(h) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int c = 0; c < kChunk; ++c) {
             const int h = h0 + 4 * c + grp;
-            if (h0 + 4 * c >= n_heads) break;          // no group of the wave has this head (uniform)
+            if (h0 + 4 * c >= hi) break;               // no group of the wave has this head (uniform)
             const u32x4 res = norm_rope_apply(x[c], go, gp, eps, cv, sv, sub);
-            if (h < n_heads) store(h, res);
+            if (h < hi) store(h, res);
         }
     }
 }
 
-// 4 tokens per 256-thread block, one per wave.
+// 4 waves per 256-thread block; wave w handles token w / chunks, heads
+// [hpw * (w % chunks), hpw * (w % chunks + 1)) of the token's hq + hkv heads.
 __global__ void __launch_bounds__(256) qk_norm_rope_kernel(
     const uint16_t* q, int64_t q_row_stride, const uint16_t* k, int64_t k_row_stride,  // may alias the outputs
     uint16_t* q_out, uint16_t* k_out, const int64_t* __restrict__ positions, int32_t n_tokens, int32_t hq,
     int32_t hkv, const uint16_t* __restrict__ gq, const uint16_t* __restrict__ gk, float eps,
-    const float* __restrict__ table, int32_t max_pos) {
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const float* __restrict__ table, int32_t max_pos, int32_t hpw, int32_t chunks) {
+    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t t = w / chunks;
     if (t >= n_tokens) return;                       // the whole wave leaves together
+    const int lo = hpw * (int)(w - t * chunks), hi = lo + hpw;
     const int lane = threadIdx.x & 63, grp = lane >> 4, sub = lane & 15;
     float cv[8], sv[8];
     load_cos_sin(rope_row(table, positions, t, max_pos), sub, cv, sv);
-    const uint16_t* qt = q + t * q_row_stride + sub * 8;
-    uint16_t* qo = q_out + t * hq * kHeadDim + sub * 8;
-    norm_rope_heads(hq, grp, sub, ldg128(gq + sub * 8), ldg128(gq + (sub ^ 8) * 8), eps, cv, sv,
-                    [&](int h) { return ldg128(qt + (int64_t)h * kHeadDim); },
-                    [&](int h, u32x4 r) { stg128(qo + (int64_t)h * kHeadDim, r); });
-    const uint16_t* kt = k + t * k_row_stride + sub * 8;
-    uint16_t* ko = k_out + t * hkv * kHeadDim + sub * 8;
-    norm_rope_heads(hkv, grp, sub, ldg128(gk + sub * 8), ldg128(gk + (sub ^ 8) * 8), eps, cv, sv,
-                    [&](int h) { return ldg128(kt + (int64_t)h * kHeadDim); },
-                    [&](int h, u32x4 r) { stg128(ko + (int64_t)h * kHeadDim, r); });
+    if (lo < hq) {
+        const uint16_t* qt = q + t * q_row_stride + sub * 8;
+        uint16_t* qo = q_out + t * hq * kHeadDim + sub * 8;
+        norm_rope_heads(lo, min(hi, hq), grp, sub, ldg128(gq + sub * 8), ldg128(gq + (sub ^ 8) * 8), eps, cv, sv,
+                        [&](int h) { return ldg128(qt + (int64_t)h * kHeadDim); },
+                        [&](int h, u32x4 r) { stg128(qo + (int64_t)h * kHeadDim, r); });
+    }
+    if (hi > hq) {
+        const uint16_t* kt = k + t * k_row_stride + sub * 8;
+        uint16_t* ko = k_out + t * hkv * kHeadDim + sub * 8;
+        norm_rope_heads(max(lo, hq) - hq, min(hi, hq + hkv) - hq, grp, sub, ldg128(gk + sub * 8),
+                        ldg128(gk + (sub ^ 8) * 8), eps, cv, sv,
+                        [&](int h) { return ldg128(kt + (int64_t)h * kHeadDim); },
+                        [&](int h, u32x4 r) { stg128(ko + (int64_t)h * kHeadDim, r); });
+    }
 }
 
-// QK-Norm + RoPE fused with the cache scatter, one token per wave.  Query
-// heads go to q_out; rotated key heads go straight to k_cache row
-// slot_mapping[t] (and to k_out when it is given); value heads are copied to
-// v_cache row slot_mapping[t].  A slot outside [0, num_slots) (the padding id
-// -1 included) writes no cache row.
+// QK-Norm + RoPE fused with the cache scatter; wave layout as above over the
+// token's hq + 2 hkv heads.  Query heads go to q_out; rotated key heads go
+// straight to k_cache row slot_mapping[t] (and to k_out when it is given);
+// value heads are copied to v_cache row slot_mapping[t].  A slot outside
+// [0, num_slots) (the padding id -1 included) writes no cache row.
 __global__ void __launch_bounds__(256) qk_norm_rope_store_kernel(
     const uint16_t* q, int64_t q_row_stride, const uint16_t* k, int64_t k_row_stride,
     const uint16_t* __restrict__ v, int64_t v_row_stride, uint16_t* q_out, uint16_t* k_out,
     uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache, int64_t num_slots,
     const int32_t* __restrict__ slot_mapping, const int64_t* __restrict__ positions, int32_t n_tokens, int32_t hq,
     int32_t hkv, const uint16_t* __restrict__ gq, const uint16_t* __restrict__ gk, float eps,
-    const float* __restrict__ table, int32_t max_pos) {
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const float* __restrict__ table, int32_t max_pos, int32_t hpw, int32_t chunks) {
+    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t t = w / chunks;
     if (t >= n_tokens) return;
+    const int lo = hpw * (int)(w - t * chunks), hi = lo + hpw;
     const int lane = threadIdx.x & 63, grp = lane >> 4, sub = lane & 15;
     const int64_t D = (int64_t)hkv * kHeadDim;
     const int64_t slot = (int64_t)slot_mapping[t];
@@ -190,38 +203,58 @@ __global__ void __launch_bounds__(256) qk_norm_rope_store_kernel(
     uint16_t* kc = to_cache ? k_cache + slot * D + sub * 8 : nullptr;
 
     // value heads: plain copies into the cache row
-    if (to_cache) {
+    const int vlo = max(lo, hq + hkv) - hq - hkv, vhi = min(hi, hq + 2 * hkv) - hq - hkv;
+    if (to_cache && vlo < vhi) {
         const uint16_t* vt = v + t * v_row_stride + sub * 8;
         uint16_t* vc = v_cache + slot * D + sub * 8;
-        for (int h0 = 0; h0 < hkv; h0 += 4 * kChunk) {
+        for (int h0 = vlo; h0 < vhi; h0 += 4 * kChunk) {
             u32x4 x[kChunk];
 #pragma unroll
             for (int c = 0; c < kChunk; ++c) {
                 const int h = h0 + 4 * c + grp;
-                if (h < hkv) x[c] = ldg128(vt + (int64_t)h * kHeadDim);
+                if (h < vhi) x[c] = ldg128(vt + (int64_t)h * kHeadDim);
             }
 #pragma unroll
             for (int c = 0; c < kChunk; ++c) {
                 const int h = h0 + 4 * c + grp;
-                if (h < hkv) stg128(vc + (int64_t)h * kHeadDim, x[c]);
+                if (h < vhi) stg128(vc + (int64_t)h * kHeadDim, x[c]);
             }
         }
     }
+    if (lo >= hq + hkv) return;
     float cv[8], sv[8];
     load_cos_sin(rope_row(table, positions, t, max_pos), sub, cv, sv);
-    const uint16_t* qt = q + t * q_row_stride + sub * 8;
-    uint16_t* qo = q_out + t * hq * kHeadDim + sub * 8;
-    norm_rope_heads(hq, grp, sub, ldg128(gq + sub * 8), ldg128(gq + (sub ^ 8) * 8), eps, cv, sv,
-                    [&](int h) { return ldg128(qt + (int64_t)h * kHeadDim); },
-                    [&](int h, u32x4 r) { stg128(qo + (int64_t)h * kHeadDim, r); });
-    const uint16_t* kt = k + t * k_row_stride + sub * 8;
-    uint16_t* ko = k_out ? k_out + t * hkv * kHeadDim + sub * 8 : nullptr;
-    norm_rope_heads(hkv, grp, sub, ldg128(gk + sub * 8), ldg128(gk + (sub ^ 8) * 8), eps, cv, sv,
-                    [&](int h) { return ldg128(kt + (int64_t)h * kHeadDim); },
-                    [&](int h, u32x4 r) {
-                        if (ko) stg128(ko + (int64_t)h * kHeadDim, r);
-                        if (kc) stg128(kc + (int64_t)h * kHeadDim, r);
-                    });
+    if (lo < hq) {
+        const uint16_t* qt = q + t * q_row_stride + sub * 8;
+        uint16_t* qo = q_out + t * hq * kHeadDim + sub * 8;
+        norm_rope_heads(lo, min(hi, hq), grp, sub, ldg128(gq + sub * 8), ldg128(gq + (sub ^ 8) * 8), eps, cv, sv,
+                        [&](int h) { return ldg128(qt + (int64_t)h * kHeadDim); },
+                        [&](int h, u32x4 r) { stg128(qo + (int64_t)h * kHeadDim, r); });
+    }
+    if (hi > hq) {
+        const uint16_t* kt = k + t * k_row_stride + sub * 8;
+        uint16_t* ko = k_out ? k_out + t * hkv * kHeadDim + sub * 8 : nullptr;
+        norm_rope_heads(max(lo, hq) - hq, min(hi, hq + hkv) - hq, grp, sub, ldg128(gk + sub * 8),
+                        ldg128(gk + (sub ^ 8) * 8), eps, cv, sv,
+                        [&](int h) { return ldg128(kt + (int64_t)h * kHeadDim); },
+                        [&](int h, u32x4 r) {
+                            if (ko) stg128(ko + (int64_t)h * kHeadDim, r);
+                            if (kc) stg128(kc + (int64_t)h * kHeadDim, r);
+                        });
+    }
+}
+
+// Heads per wave: all of a token's heads once there are enough tokens to fill
+// the device (2048 waves, 8 per CU); fewer tokens split each token's heads
+// into chunks (a multiple of 4, at least 4) so the launch still has ~2048 waves.
+static void heads_per_wave(int64_t n_tokens, int heads, int32_t& hpw, int32_t& chunks) {
+    const int64_t target = 2048;
+    int64_t want = (heads * n_tokens + target - 1) / target;   // heads per wave for ~target waves
+    want = (want + 3) / 4 * 4;
+    if (want < 4) want = 4;
+    if (want > heads) want = (heads + 3) / 4 * 4;
+    hpw = (int32_t)want;
+    chunks = (heads + hpw - 1) / hpw;
 }
 
 hipError_t launch_qk_norm_rope(const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride,
@@ -229,11 +262,13 @@ hipError_t launch_qk_norm_rope(const void* q, int64_t q_row_stride, const void* 
                                int32_t hq, int32_t hkv, const void* gq, const void* gk, float eps,
                                const float* table, int32_t max_pos, hipStream_t stream) {
     if (n_tokens == 0) return hipSuccess;
-    const int64_t blocks = ((int64_t)n_tokens + 3) / 4;
+    int32_t hpw, chunks;
+    heads_per_wave(n_tokens, hq + hkv, hpw, chunks);
+    const int64_t blocks = ((int64_t)n_tokens * chunks + 3) / 4;
     hipLaunchKernelGGL(qk_norm_rope_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        (const uint16_t*)q, q_row_stride, (const uint16_t*)k, k_row_stride, (uint16_t*)q_out,
                        (uint16_t*)k_out, positions, n_tokens, hq, hkv, (const uint16_t*)gq, (const uint16_t*)gk,
-                       eps, table, max_pos);
+                       eps, table, max_pos, hpw, chunks);
     return hipGetLastError();
 }
 
@@ -244,12 +279,14 @@ hipError_t launch_qk_norm_rope_store(const void* q, int64_t q_row_stride, const 
                                      const void* gq, const void* gk, float eps, const float* table, int32_t max_pos,
                                      hipStream_t stream) {
     if (n_tokens == 0) return hipSuccess;
-    const int64_t blocks = ((int64_t)n_tokens + 3) / 4;
+    int32_t hpw, chunks;
+    heads_per_wave(n_tokens, hq + 2 * hkv, hpw, chunks);
+    const int64_t blocks = ((int64_t)n_tokens * chunks + 3) / 4;
     hipLaunchKernelGGL(qk_norm_rope_store_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const uint16_t*)q,
                        q_row_stride, (const uint16_t*)k, k_row_stride, (const uint16_t*)v, v_row_stride,
                        (uint16_t*)q_out, (uint16_t*)k_out, (uint16_t*)k_cache, (uint16_t*)v_cache, num_slots,
                        slot_mapping, positions, n_tokens, hq, hkv, (const uint16_t*)gq, (const uint16_t*)gk, eps,
-                       table, max_pos);
+                       table, max_pos, hpw, chunks);
     return hipGetLastError();
 }
 
