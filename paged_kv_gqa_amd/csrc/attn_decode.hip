@@ -276,9 +276,11 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
 }
 
 // Dispatch order of the split items (b, s): a counting sort by the number of
-// blocks the item covers, largest first, empty items last (one workgroup; items
-// of equal size in any order -- the order only schedules work, every result is
-// the same).
+// blocks the item covers, largest first, empty items last (one workgroup).
+// Items are entered split-major, so within a size class the first splits of
+// all sequences come first and the reads of a prefix that several sequences
+// share fall close together in time.  The order only schedules work: every
+// result is the same.
 __global__ void __launch_bounds__(1024) decode_order_kernel(const int32_t* __restrict__ context_lens,
                                                             int32_t max_blocks, int32_t num_seqs, int32_t split_blocks,
                                                             int32_t max_splits, int32_t* __restrict__ work) {
@@ -306,7 +308,11 @@ __global__ void __launch_bounds__(1024) decode_order_kernel(const int32_t* __res
         }
     }
     __syncthreads();
-    for (int it = tid; it < n_items; it += 1024) work[atomicAdd(&s_bin[key(it)], 1)] = it;
+    for (int j = tid; j < n_items; j += 1024) {
+        const int s = j / num_seqs, b = j - s * num_seqs;
+        const int it = b * max_splits + s;
+        work[atomicAdd(&s_bin[key(it)], 1)] = it;
+    }
 }
 
 // One workgroup of 128 threads per (b, h): merge the splits in order.  The
