@@ -240,6 +240,7 @@ def main():
 
     ops = sublayer_ops(pkv, torch, dev, to_dev, args, log)
     norm_small = norm_rope_small(pkv, torch, dev, table, args, log)
+    small = small_configs(pkv, torch, dev, to_dev, args, log)
     copy_ref = copy_reference(torch, dev, log)
 
     ladder = decode_graph_ladder(pkv, torch, s8, table, qkv_d, kc_d, vc_d, pos_d, slot_d, cl_d, bt_d, gq_d, gk_d,
@@ -284,6 +285,7 @@ def main():
         "cpu_baseline": cpu,
         "sublayer_ops": ops,
         "qk_norm_rope_small": norm_small,
+        "qwen3_0_6b": small,
         "decode_graph": ladder,
         "cpu_baseline_prefill": cpu_pre,
     }
@@ -315,6 +317,62 @@ def copy_reference(torch, dev, log):
     out = {"copy_GB/s": round(2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9, 1)}
     log(f"streaming reference: {out}")
     del src, dst
+    return out
+
+
+def small_configs(pkv, torch, dev, to_dev, args, log):
+    """Secondary numbers at the Qwen3-0.6B head counts (16 q / 8 kv): the varlen causal
+    prefill on fresh K/V (8 sequences, lengths U[128, 2048]; small enough that launch and
+    tail dominate) and the paged decode of 64 sequences (contexts U[512, 8192]).  Each
+    attention call is timed alone with events over args.steps launches."""
+    import workloads as wl
+    D = 128
+    out = {}
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / args.steps
+
+    w2 = wl.varlen_prefill(args.seed)
+    s6 = w2.shape
+    q0, k0, v0 = wl.qkv_views(s6)
+    qkv = to_dev(w2.qkv())
+    T = qkv.shape[0]
+    q = qkv[:, q0:k0].view(T, s6.num_q_heads, D)
+    k = qkv[:, k0:v0].view(T, s6.num_kv_heads, D)
+    v = qkv[:, v0:].view(T, s6.num_kv_heads, D)
+    cu = to_dev(w2.cu_seqlens)
+    L = int(w2.lengths.max())
+    o = torch.empty((T, s6.num_q_heads, D), dtype=torch.bfloat16, device=dev)
+    ms = timed(lambda: pkv.attn_prefill_varlen(q, k, v, cu, cu, L, L, out=o))
+    out["varlen_prefill"] = {"tokens": T, "lengths": [int(x) for x in w2.lengths], "ms": round(ms, 4),
+                             "TFLOP/s": round(w2.flops / (ms * 1e-3) / 1e12, 2)}
+    del qkv, o
+
+    w3 = wl.paged_decode_0_6b(args.seed)
+    hkv, hq = w3.shape.num_kv_heads, w3.shape.num_q_heads
+    kc = torch.empty((w3.num_blocks, 256, hkv, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    wl.fill_normal_bf16_(kc, 3, args.seed, 10)
+    wl.fill_normal_bf16_(vc, 3, args.seed, 11)
+    qd, cl, bt = to_dev(w3.q()), to_dev(w3.context_lens), to_dev(w3.block_tables)
+    ws = torch.empty(pkv.decode_workspace_bytes(w3.batch, hq, hkv, w3.block_tables.shape[1]), dtype=torch.uint8,
+                     device=dev)
+    od = torch.empty((w3.batch, hq, D), dtype=torch.bfloat16, device=dev)
+    ms = timed(lambda: pkv.attn_decode_paged(qd, kc, vc, cl, bt, out=od, workspace=ws))
+    nbytes = w3.algorithmic_bytes()
+    out["paged_decode"] = {"batch": w3.batch, "ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 2),
+                           "bytes": nbytes}
+    log(f"qwen3-0.6b shapes: {json.dumps(out)}")
+    del kc, vc
     return out
 
 

@@ -37,8 +37,9 @@
 //     a row grows by more than 2^8, so the O rescale is skipped on most tiles.
 //   * Causal tile skipping: a wave stops at the tile holding its last visible
 //     key; only tiles that cross the diagonal (or the sequence end) are masked.
-//   * Work order: longest query blocks first inside each (sequence, kv head),
-//     and consecutive work items share an XCD so their K/V stays in its L2.
+//   * Work order: longest query blocks first inside each (sequence, kv head);
+//     each such unit runs on one XCD (its K/V stays in that L2) and the units
+//     are dealt round-robin over the 8 XCDs, so unequal sequences balance.
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -72,7 +73,13 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a,
     __shared__ __attribute__((aligned(16))) unsigned char k_lds[2 * kKTileBytes];
     __shared__ __attribute__((aligned(16))) unsigned char v_lds[2 * kVTileBytes];
 
-    const int work = xcd_remap(blockIdx.x, n_work);
+    // Work units of m_blocks consecutive items (one sequence, kv head and head
+    // group: all its query blocks) are dealt round-robin over the 8 XCDs, which
+    // take workgroups round-robin by id: XCD x runs units x, x+8, x+16, ... in
+    // order, so a unit's K/V stays in one L2 while a batch of unequal sequences
+    // still spreads evenly over the XCDs.
+    const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
+    const int work = (xcd + 8 * (kx / m_blocks)) * m_blocks + kx % m_blocks;
     if (work >= n_work) return;
     // work = ((b * hkv + g) * head_groups + hg) * m_blocks + (m_blocks - 1 - mb)
     const int mb = m_blocks - 1 - (work % m_blocks);
@@ -341,7 +348,10 @@ hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t stream) {
     const int64_t n_work64 = (int64_t)a.num_seqs * a.hkv * head_groups * m_blocks;
     if (n_work64 > (int64_t)0x7FFFFFF0) return hipErrorInvalidValue;
     const int n_work = (int)n_work64;
-    const int grid = ((n_work + 7) / 8) * 8;
+    const int64_t units = n_work64 / m_blocks;
+    const int64_t grid64 = ((units + 7) / 8) * 8 * m_blocks;
+    if (grid64 > (int64_t)0x7FFFFFF0) return hipErrorInvalidValue;
+    const int grid = (int)grid64;
     const bool paged = a.block_table != nullptr;
 #define PKV_PREFILL(GW_, PG_, NW_)                                                                               \
     hipLaunchKernelGGL((prefill_kernel<GW_, PG_, NW_>), dim3(grid), dim3(64 * NW_), 0, stream, a, m_blocks, n_work, \

@@ -43,15 +43,4 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// Launch-order remap so that consecutive work items land on the same XCD.
-// Workgroups are dispatched round-robin over the 8 XCDs: id -> XCD id % 8.
-// Item k of XCD x's share gets work index x * per + k.  Ids past the share
-// sizes map to >= n and are skipped by the caller.
-__device__ __forceinline__ int xcd_remap(int id, int n) {
-    const int per = (n + 7) >> 3;
-    const int x = id & 7;
-    const int k = id >> 3;
-    return x * per + k;
-}
-
 }  // namespace pkv
