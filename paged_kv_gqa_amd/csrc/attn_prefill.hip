@@ -39,7 +39,8 @@
 //     key; only tiles that cross the diagonal (or the sequence end) are masked.
 //   * Work order: longest query blocks first inside each (sequence, kv head);
 //     each such unit runs on one XCD (its K/V stays in that L2) and the units
-//     are dealt round-robin over the 8 XCDs, so unequal sequences balance.
+//     are dealt round-robin over the 8 XCDs (cut into 2-block chunks when there
+//     are fewer than 8), so unequal or few sequences balance.
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -57,7 +58,7 @@ constexpr float kLazyLog2 = 8.0f;           // the lazy reference max moves when
 // workgroups of 4 per CU, or one of 8).
 template <int GW, bool PAGED, int NW>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a, int32_t m_blocks, int32_t n_work,
-                                                                  int32_t head_groups) {
+                                                                  int32_t head_groups, int32_t chunk) {
     constexpr int kThreads = 64 * NW;
     // Keys per tile: 128 for the 8-wave workgroup (one per CU, LDS for two 74 KB
     // tile pairs), 64 for 4 waves (two workgroups per CU).  A tile never
@@ -73,13 +74,14 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a,
     __shared__ __attribute__((aligned(16))) unsigned char k_lds[2 * kKTileBytes];
     __shared__ __attribute__((aligned(16))) unsigned char v_lds[2 * kVTileBytes];
 
-    // Work units of m_blocks consecutive items (one sequence, kv head and head
-    // group: all its query blocks) are dealt round-robin over the 8 XCDs, which
-    // take workgroups round-robin by id: XCD x runs units x, x+8, x+16, ... in
-    // order, so a unit's K/V stays in one L2 while a batch of unequal sequences
-    // still spreads evenly over the XCDs.
+    // Chunks of `chunk` consecutive work items are dealt round-robin over the 8
+    // XCDs, which take workgroups round-robin by id: XCD x runs chunks x, x+8,
+    // x+16, ... in order.  A chunk is one (sequence, kv head, head group) unit --
+    // all its query blocks, so its K/V stays in one L2 -- unless there are fewer
+    // units than XCDs; then it is two query blocks, so few sequences still spread
+    // over all XCDs.
     const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
-    const int work = (xcd + 8 * (kx / m_blocks)) * m_blocks + kx % m_blocks;
+    const int work = (xcd + 8 * (kx / chunk)) * chunk + kx % chunk;
     if (work >= n_work) return;
     // work = ((b * hkv + g) * head_groups + hg) * m_blocks + (m_blocks - 1 - mb)
     const int mb = m_blocks - 1 - (work % m_blocks);
@@ -348,14 +350,18 @@ hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t stream) {
     const int64_t n_work64 = (int64_t)a.num_seqs * a.hkv * head_groups * m_blocks;
     if (n_work64 > (int64_t)0x7FFFFFF0) return hipErrorInvalidValue;
     const int n_work = (int)n_work64;
+    // Whole units (all query blocks of a sequence and kv head) per XCD keep their
+    // K/V in one L2; with fewer units than XCDs they are cut into 2-block chunks.
     const int64_t units = n_work64 / m_blocks;
-    const int64_t grid64 = ((units + 7) / 8) * 8 * m_blocks;
+    const int64_t chunk = units >= 8 ? m_blocks : (m_blocks < 2 ? m_blocks : 2);
+    const int64_t n_chunks = (n_work64 + chunk - 1) / chunk;
+    const int64_t grid64 = ((n_chunks + 7) / 8) * 8 * chunk;
     if (grid64 > (int64_t)0x7FFFFFF0) return hipErrorInvalidValue;
     const int grid = (int)grid64;
     const bool paged = a.block_table != nullptr;
 #define PKV_PREFILL(GW_, PG_, NW_)                                                                               \
     hipLaunchKernelGGL((prefill_kernel<GW_, PG_, NW_>), dim3(grid), dim3(64 * NW_), 0, stream, a, m_blocks, n_work, \
-                       head_groups)
+                       head_groups, (int32_t)chunk)
     if (gw == 4) {
         if (paged) PKV_PREFILL(4, true, 8); else PKV_PREFILL(4, false, 8);
     } else if (gw == 2) {

@@ -222,6 +222,16 @@ def test_prefill_varlen_ragged(dev, hq, hkv):
     check_attn(f64(o), ref, "prefill ragged")
 
 
+@pytest.mark.parametrize("lens,hq,hkv", [([1500], 4, 1), ([700, 90, 333], 4, 2), ([257], 8, 1)])
+def test_prefill_few_work_units(dev, lens, hq, hkv):
+    """Fewer (sequence, kv head) units than XCDs: the work is dealt in 2-block chunks."""
+    _say(f"prefill case 1, lengths {lens}, {hq}/{hkv} heads (fewer than 8 units)")
+    o, ref, _ = _prefill_case(dev, lens, lens, hq, hkv, seed=sum(lens) + hq)
+    check_attn(f64(o), ref, "prefill few units")
+    o2, ref2, _ = _prefill_case(dev, [min(64, L) for L in lens], lens, hq, hkv, seed=sum(lens), paged=True)
+    check_attn(f64(o2), ref2, "prefill few units, paged")
+
+
 def test_prefill_paged_prefix(dev):
     lk, lq = [300, 513, 64, 1000], [40, 257, 64, 1]
     _say(f"prefill case 2 (paged), Lk {lk}, Lq {lq}")
