@@ -246,10 +246,11 @@ def main():
     ladder = decode_graph_ladder(pkv, torch, s8, table, qkv_d, kc_d, vc_d, pos_d, slot_d, cl_d, bt_d, gq_d, gk_d,
                                  args, log)
 
-    cpu = cpu_pre = None
+    cpu = cpu_pre = cpu_st = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, wd, kc_d, vc_d, qo_d, log)
         cpu_pre = cpu_baseline_prefill(args, wp, kc_p, vc_p, qo_p, log)
+        cpu_st = cpu_stages(args, wp, qkv_p, log)
 
     out = {
         "metric": METRIC,
@@ -288,6 +289,7 @@ def main():
         "qwen3_0_6b": small,
         "decode_graph": ladder,
         "cpu_baseline_prefill": cpu_pre,
+        "cpu_baseline_stages": cpu_st,
     }
     print(json.dumps(out), flush=True)
 
@@ -490,6 +492,53 @@ def decode_graph_ladder(pkv, torch, s8, table, qkv_d, kc_d, vc_d, pos_d, slot_d,
     return out
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_stages(args, wp, qkv_p, log):
+    """The oracle's first two steps on the first 4096 tokens of the prefix-hit prefill:
+    QK-Norm + RoPE of q and k, then the scatter of k' and v into a host cache.  GB/s of the
+    same algorithmic bytes the GPU kernels are credited with."""
+    import torch
+
+    import oracle
+    import workloads as wl
+    s8 = wl.QWEN3_8B
+    n = min(4096, wp.num_q_tokens)
+    qkv = qkv_p[:n].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    q0, k0, v0 = wl.qkv_views(s8)
+    gq, gk = wp.gammas()
+    pos = np.ascontiguousarray(wp.positions[:n])
+    table = oracle.rope_table(s8.max_position, 128, s8.rope_theta)
+    t0 = time.perf_counter()
+    oracle.rmsnorm_rope(qkv, s8.num_q_heads, 128, gq, s8.eps, pos, table, col_offset=q0)
+    kr = oracle.rmsnorm_rope(qkv, s8.num_kv_heads, 128, gk, s8.eps, pos, table, col_offset=k0)
+    t_norm = time.perf_counter() - t0
+    kb = oracle.round_bf16(kr)
+    vb = np.ascontiguousarray(qkv[:, v0:]).reshape(n, s8.num_kv_heads, 128)
+    kc = np.zeros((wp.num_blocks * 256, s8.num_kv_heads, 128), np.uint16)
+    vc = np.zeros_like(kc)
+    t0 = time.perf_counter()
+    oracle.store_kvcache(kb, vb, kc, vc, np.ascontiguousarray(wp.slot_mapping[:n]))
+    t_store = time.perf_counter() - t0
+    norm_bytes = n * ((s8.num_q_heads + s8.num_kv_heads) * 128 * 2 * 2 + 8 + 512)
+    store_bytes = n * (2 * 2 * 2 * s8.num_kv_heads * 128 + 4)
+    out = {"qk_norm_rope": {"value": round(norm_bytes / t_norm / 1e9, 4), "unit": "GB/s", "s": round(t_norm, 3)},
+           "store_kvcache": {"value": round(store_bytes / t_store / 1e9, 4), "unit": "GB/s", "s": round(t_store, 3)},
+           "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": f"first {n} tokens of the prefix-hit prefill, 32/8 heads, fp64 C oracle"}
+    log(f"cpu stages: {json.dumps(out)}")
+    return out
+
+
 def cpu_baseline(args, wd, kc_d, vc_d, q_d, log):
     """The oracle's paged decode over the decode workload's sequences, on the host cores.
 
@@ -531,6 +580,7 @@ def cpu_baseline(args, wd, kc_d, vc_d, q_d, log):
         del kc, vc
     log(f"cpu baseline: {n} sequences, {nbytes / 1e9:.3f} GB in {total:.2f} s")
     return {"value": round(nbytes / total / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"paged decode of {n} of the {wd.batch} sequences ({toks} context tokens, {hq}/{hkv} heads), "
                       f"fp64 C oracle with OpenMP, {total:.2f} s of oracle time (K/V read per sequence, "
                       f"shared prefix counted per sequence)"}
