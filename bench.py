@@ -504,7 +504,7 @@ def cpu_model():
 
 
 def cpu_stages(args, wp, qkv_p, log):
-    """The oracle's first two steps on the first 4096 tokens of the prefix-hit prefill:
+    """The oracle's first two steps on the first 16384 tokens of the prefix-hit prefill:
     QK-Norm + RoPE of q and k, then the scatter of k' and v into a host cache.  GB/s of the
     same algorithmic bytes the GPU kernels are credited with."""
     import torch
@@ -512,7 +512,7 @@ def cpu_stages(args, wp, qkv_p, log):
     import oracle
     import workloads as wl
     s8 = wl.QWEN3_8B
-    n = min(4096, wp.num_q_tokens)
+    n = min(16384, wp.num_q_tokens)
     qkv = qkv_p[:n].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     q0, k0, v0 = wl.qkv_views(s8)
     gq, gk = wp.gammas()
