@@ -240,7 +240,7 @@ def main():
 
     ops = sublayer_ops(pkv, torch, dev, to_dev, args, log)
     norm_small = norm_rope_small(pkv, torch, dev, table, args, log)
-    small = small_configs(pkv, torch, dev, to_dev, args, log)
+    small = qwen3_0_6b_shapes(pkv, torch, dev, to_dev, args, log)
     copy_ref = copy_reference(torch, dev, log)
 
     ladder = decode_graph_ladder(pkv, torch, s8, table, qkv_d, kc_d, vc_d, pos_d, slot_d, cl_d, bt_d, gq_d, gk_d,
@@ -322,7 +322,7 @@ def copy_reference(torch, dev, log):
     return out
 
 
-def small_configs(pkv, torch, dev, to_dev, args, log):
+def qwen3_0_6b_shapes(pkv, torch, dev, to_dev, args, log):
     """Secondary numbers at the Qwen3-0.6B head counts (16 q / 8 kv): the varlen causal
     prefill on fresh K/V (8 sequences, lengths U[128, 2048]; small enough that launch and
     tail dominate) and the paged decode of 64 sequences (contexts U[512, 8192]).  Each
