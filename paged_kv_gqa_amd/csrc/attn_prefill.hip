@@ -19,9 +19,11 @@
 //     lane 32 away.  The S^T accumulator is, after exp2 and bf16 packing,
 //     already the B operand of the PV product.
 //   * A workgroup owns one kv head and the query heads of its GQA group that
-//     share it; each wave computes 32 query rows of one head.  With groups of
-//     4 the workgroup has 8 waves (4 heads x 64 positions) and each K/V tile
-//     staged in LDS feeds 256 query rows; smaller groups use 4 waves.  K and V are both kept row-major in LDS
+//     share it; each wave computes 32 query rows of one head.  For batches of
+//     long sequences (mean query length >= 1024) the workgroup has 8 waves
+//     (4 heads x 64 positions, or 2 x 128) and 128-key tiles, so each K/V tile
+//     staged in LDS feeds 256 query rows; otherwise 4 waves and 64-key tiles
+//     (more, smaller workgroups).  K and V are both kept row-major in LDS
 //     (plain 16-byte copies, padded rows: no bank conflicts); the PV product
 //     needs V transposed, which the gfx950 transposing LDS read
 //     (ds_read_b64_tr_b16) delivers: lane j of a 16-lane group addresses key
@@ -344,7 +346,10 @@ hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t stream) {
     const int head_groups = G / gw;
     // Four query heads share each K/V tile across 8 waves (64 positions); smaller
     // groups keep 4 waves so short sequences still spread over many workgroups.
-    const int nw = gw == 4 ? 8 : 4;
+    // 8 waves (64 positions x 4 heads, or 128 x 2, 128-key tiles) for long
+    // sequences; 4 waves (smaller workgroups, more of them) for short ones
+    const bool wide = gw >= 2 && (int64_t)a.total_q >= (int64_t)1024 * a.num_seqs;
+    const int nw = wide ? 8 : 4;
     const int bm = kRowsPerWave * (nw / gw);
     const int m_blocks = (a.max_seqlen_q + bm - 1) / bm;
     const int64_t n_work64 = (int64_t)a.num_seqs * a.hkv * head_groups * m_blocks;
@@ -363,9 +368,17 @@ hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((prefill_kernel<GW_, PG_, NW_>), dim3(grid), dim3(64 * NW_), 0, stream, a, m_blocks, n_work, \
                        head_groups, (int32_t)chunk)
     if (gw == 4) {
-        if (paged) PKV_PREFILL(4, true, 8); else PKV_PREFILL(4, false, 8);
+        if (wide) {
+            if (paged) PKV_PREFILL(4, true, 8); else PKV_PREFILL(4, false, 8);
+        } else {
+            if (paged) PKV_PREFILL(4, true, 4); else PKV_PREFILL(4, false, 4);
+        }
     } else if (gw == 2) {
-        if (paged) PKV_PREFILL(2, true, 4); else PKV_PREFILL(2, false, 4);
+        if (wide) {
+            if (paged) PKV_PREFILL(2, true, 8); else PKV_PREFILL(2, false, 8);
+        } else {
+            if (paged) PKV_PREFILL(2, true, 4); else PKV_PREFILL(2, false, 4);
+        }
     } else if (gw == 1) {
         if (paged) PKV_PREFILL(1, true, 4); else PKV_PREFILL(1, false, 4);
     } else {

@@ -222,6 +222,19 @@ def test_prefill_varlen_ragged(dev, hq, hkv):
     check_attn(f64(o), ref, "prefill ragged")
 
 
+@pytest.mark.parametrize("lens,hq,hkv", [([1100, 1500, 1025, 1300], 16, 8), ([1200, 2100], 32, 8), ([1024] * 3, 8, 4)])
+def test_prefill_long_sequences_wide_workgroups(dev, lens, hq, hkv):
+    """Mean query length >= 1024: 8-wave workgroups with 128-key tiles for every GQA group size."""
+    _say(f"prefill case 1, lengths {lens}, {hq}/{hkv} heads (8-wave workgroups)")
+    rows = np.stack([np.arange(0, sum(lens), 7), np.arange(0, sum(lens), 7) % hq], 1)
+    o, ref, _ = _prefill_case(dev, lens, lens, hq, hkv, seed=len(lens) + hq, rows=rows)
+    check_attn(f64(o)[rows[:, 0], rows[:, 1]], ref, "prefill long, 8 waves")
+    lq = [L - 37 for L in lens]
+    rows = np.stack([np.arange(0, sum(lq), 5), np.arange(0, sum(lq), 5) % hq], 1)
+    o2, ref2, _ = _prefill_case(dev, lq, lens, hq, hkv, seed=len(lens), paged=True, rows=rows)
+    check_attn(f64(o2)[rows[:, 0], rows[:, 1]], ref2, "prefill long paged, 8 waves")
+
+
 @pytest.mark.parametrize("lens,hq,hkv", [([1500], 4, 1), ([700, 90, 333], 4, 2), ([257], 8, 1)])
 def test_prefill_few_work_units(dev, lens, hq, hkv):
     """Fewer (sequence, kv head) units than XCDs: the work is dealt in 2-block chunks."""
