@@ -45,9 +45,11 @@ namespace pkv {
 
 namespace {
 constexpr int kDecThreads = 256;
-// Tuning (measured on MI355X, Qwen3-8B decode workload): splits of up to 8
-// blocks, a ring of 2 chunks of 16 keys per wave, 2 waves per SIMD.  Longer
-// splits amortise each workgroup's pipeline fill; deeper rings did not pay.
+// Tuning (measured on MI355X, Qwen3-8B and 0.6B decode workloads): splits of up
+// to 8 blocks, shortened one block at a time while the batch would have fewer
+// than ~1400 split items, a ring of 2 chunks of 16 keys per wave, 2 waves per
+// SIMD.  Longer splits amortise each workgroup's pipeline fill; deeper rings
+// did not pay.
 #ifndef PKV_DECODE_SPLIT
 #define PKV_DECODE_SPLIT 8
 #endif
@@ -59,7 +61,7 @@ constexpr int kDecThreads = 256;
 #endif
 constexpr int kMaxSplitBlocks = PKV_DECODE_SPLIT;   // blocks per split-K work item (at most)
 #ifndef PKV_DECODE_TARGET
-#define PKV_DECODE_TARGET 2048
+#define PKV_DECODE_TARGET 1400
 #endif
 constexpr int kTargetItems = PKV_DECODE_TARGET;
 constexpr float kLazyMax = 8.0f;   // log2 headroom of the lazy reference max
@@ -97,7 +99,7 @@ int decode_split_blocks(int32_t num_seqs, int32_t hkv, int32_t max_blocks) {
     while (sb > 1) {
         const int64_t items = (int64_t)num_seqs * ((hkv + 3) / 4) * ((max_blocks + sb - 1) / sb);
         if (items >= kTargetItems) break;
-        sb >>= 1;
+        --sb;
     }
     return sb;
 }
