@@ -222,7 +222,8 @@ def test_prefill_varlen_ragged(dev, hq, hkv):
     check_attn(f64(o), ref, "prefill ragged")
 
 
-@pytest.mark.parametrize("lens,hq,hkv", [([1100, 1500, 1025, 1300], 16, 8), ([1200, 2100], 32, 8), ([1024] * 3, 8, 4)])
+@pytest.mark.parametrize("lens,hq,hkv", [([1100, 1500, 1025, 1300], 16, 8), ([1200, 2100], 32, 8), ([1024] * 3, 8, 4),
+                                         ([1100, 1300], 64, 8), ([2048], 8, 8)])
 def test_prefill_long_sequences_wide_workgroups(dev, lens, hq, hkv):
     """Mean query length >= 1024: 8-wave workgroups with 128-key tiles for every GQA group size."""
     _say(f"prefill case 1, lengths {lens}, {hq}/{hkv} heads (8-wave workgroups)")
