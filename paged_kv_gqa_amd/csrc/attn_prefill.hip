@@ -20,7 +20,7 @@
 //     already the B operand of the PV product.
 //   * A workgroup owns one kv head and the query heads of its GQA group that
 //     share it; each wave computes 32 query rows of one head.  For batches of
-//     long sequences (mean query length >= 1024) the workgroup has 8 waves
+//     long sequences (mean query length >= 2048) the workgroup has 8 waves
 //     (4 heads x 64 positions, or 2 x 128) and 128-key tiles, so each K/V tile
 //     staged in LDS feeds 256 query rows; otherwise 4 waves and 64-key tiles
 //     (more, smaller workgroups).  K and V are both kept row-major in LDS
@@ -348,7 +348,7 @@ hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t stream) {
     // groups keep 4 waves so short sequences still spread over many workgroups.
     // 8 waves (64 positions x 4 heads, or 128 x 2, 128-key tiles) for long
     // sequences; 4 waves (smaller workgroups, more of them) for short ones
-    const bool wide = gw >= 2 && (int64_t)a.total_q >= (int64_t)1024 * a.num_seqs;
+    const bool wide = gw >= 2 && (int64_t)a.total_q >= (int64_t)2048 * a.num_seqs;
     const int nw = wide ? 8 : 4;
     const int bm = kRowsPerWave * (nw / gw);
     const int m_blocks = (a.max_seqlen_q + bm - 1) / bm;
