@@ -176,14 +176,16 @@ PKV_API int pkv_qk_norm_rope_store(const void* q, int64_t q_row_stride, const vo
  * with q head h reading kv head h / (num_q_heads / num_kv_heads).
  *
  *   block_table == NULL ("case 1", fresh K/V): key j of sequence b is row
- *       cu_seqlens_k[b] + j of k / v (row strides k_row_stride / v_row_stride).
+ *       cu_seqlens_k[b] + j of k / v (row strides k_row_stride / v_row_stride,
+ *       each at most 2^24 elements).
  *   block_table != NULL ("case 2", prefix hit or later chunk): k and v are the
  *       caches [num_blocks][block_size][num_kv_heads][head_dim]; key j of
  *       sequence b is cache row block_table[b][j / block_size] * block_size
  *       + j % block_size.  The row strides must be num_kv_heads*head_dim.
  *       num_blocks bounds the ids read (ids outside are never dereferenced).
  *   q, q_row_stride   bf16 rows of num_q_heads*head_dim elements.
- *   o                 bf16 contiguous [Tq][num_q_heads][head_dim], Tq = cu_seqlens_q[num_seqs].
+ *   o                 bf16 contiguous [Tq][num_q_heads][head_dim], Tq = cu_seqlens_q[num_seqs];
+ *                     must not overlap q.
  *   cu_seqlens_q/k    int32 [num_seqs+1], non-decreasing, starting at 0.
  *   max_seqlen_q      >= every Lq_b (sizes the launch grid); max_seqlen_k >= every Lk_b.
  *   total_q           cu_seqlens_q[num_seqs] (host copy, bounds the q/o rows touched).

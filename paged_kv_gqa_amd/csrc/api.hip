@@ -206,6 +206,14 @@ int pkv_attn_prefill_varlen(const void* q, int64_t q_row_stride, const void* k, 
                 "%s: k/v row strides must be >= num_kv_heads*head_dim", fn);
     PKV_REQUIRE(q_row_stride % 8 == 0 && k_row_stride % 8 == 0 && v_row_stride % 8 == 0, PKV_ERR_INVALID_ARG,
                 "%s: row strides must be multiples of 8 elements", fn);
+    PKV_REQUIRE(k_row_stride <= (int64_t)1 << 24 && v_row_stride <= (int64_t)1 << 24, PKV_ERR_INVALID_ARG,
+                "%s: k/v row strides must be at most 2^24 elements", fn);
+    {
+        // o must not overlap q: rows flagged by the fast pass are recomputed from q.
+        const uintptr_t q0 = (uintptr_t)q, q1 = q0 + (uintptr_t)(((int64_t)(total_q - 1) * q_row_stride + qw) * 2);
+        const uintptr_t o0 = (uintptr_t)o, o1 = o0 + (uintptr_t)((int64_t)total_q * qw * 2);
+        PKV_REQUIRE(o1 <= q0 || q1 <= o0, PKV_ERR_INVALID_ARG, "%s: o must not overlap q", fn);
+    }
     PKV_REQUIRE(((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) % 16 == 0, PKV_ERR_INVALID_ARG,
                 "%s: tensors must be 16-byte aligned", fn);
     if (block_table) {

@@ -7,17 +7,17 @@
 // With a block table the keys come from the paged cache ("case 2", prefix hit
 // or a later chunk): query i of a sequence sits at absolute position
 // Lk - Lq + i.  q head h reads kv head h / (Hq/Hkv) ("Nano-vLLM 源码解读 #17
-// 注意力层", section 3).  The softmax is the exact online form of the same
-// page's section 5.2, in base 2 with the scale folded into the exponent.
+// 注意力层", section 3).  The softmax is that of the same page's section 5.2,
+// in base 2 with the scale folded into the exponent.
 //
 // Design for CDNA4:
 //   * Transposed products keep every softmax statistic lane-local:
 //       S^T[key][q] = K . Q^T    and    O^T[d][q] += V^T . P^T
 //     on v_mfma_f32_32x32x16_bf16.  In the 32x32 accumulator layout a lane
-//     owns one column (one query row), so the running max, the rescale of O
-//     and the sum stay in registers; only the max needs one swap with the
-//     lane 32 away.  The S^T accumulator is, after exp2 and bf16 packing,
-//     already the B operand of the PV product.
+//     owns one column (one query row), so the row max, the rescale of O and
+//     the sum stay in registers; only the max needs one swap with the lane 32
+//     away.  The S^T accumulator is, after exp2 and bf16 packing, already the
+//     B operand of the PV product.
 //   * A workgroup owns one kv head and the query heads of its GQA group that
 //     share it; each wave computes 32 query rows of one head.  For batches of
 //     long sequences (mean query length >= 2048) the workgroup has 8 waves
@@ -32,17 +32,29 @@
 //   * Double-buffered LDS (one barrier per tile); the tile after next is
 //     loaded into registers while the current one is computed.  Tiles (128
 //     keys with 8 waves, 64 with 4) never straddle a 256-token block, so the
-//     paged loader does one block-table lookup per tile.  Loads are issued on every path (rows past
-//     the last key are clamped) so the compiler's wait counts stay exact.
-//   * Softmax: row max on raw scores, scale folded into one FMA ahead of the
-//     hardware exp2; the running max is a lazy reference that moves only when
-//     a row grows by more than 2^8, so the O rescale is skipped on most tiles.
+//     paged loader does one block-table lookup per tile.  Loads are issued on
+//     every path (rows past the last key are clamped) so the compiler's wait
+//     counts stay exact.
+//   * Softmax in two passes.  The fast pass (one kernel) pre-scales Q by
+//     softmax_scale * log2(e) and takes exp2 of each score against a fixed
+//     reference of 0: no row max, no rescale, three VALU operations per score
+//     (exp2, add, half a bf16 pack) instead of five.  The reference cancels in
+//     O / l, so this is exact up to rounding while a row's weights stay far
+//     from overflow and underflow; a wave whose rows leave l in [2^-64, 2^64]
+//     (or whose O is not finite) writes a marker instead of its results.  The
+//     exact pass (a second, persistent kernel) recomputes only flagged work
+//     items, with Q as given, the scale in fp32, and an online running max that
+//     moves only when a row grows by more than 2^8.  A call with nothing
+//     flagged costs one short launch whose workgroups read one word and exit.
 //   * Causal tile skipping: a wave stops at the tile holding its last visible
 //     key; only tiles that cross the diagonal (or the sequence end) are masked.
 //   * Work order: longest query blocks first inside each (sequence, kv head);
 //     each such unit runs on one XCD (its K/V stays in that L2) and the units
 //     are dealt round-robin over the 8 XCDs (cut into 2-block chunks when there
 //     are fewer than 8), so unequal or few sequences balance.
+#include <algorithm>
+#include <atomic>
+
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -50,22 +62,39 @@ namespace pkv {
 
 namespace {
 typedef __attribute__((address_space(3))) bf16x4* lds_ptr_t;
+typedef __attribute__((address_space(3))) unsigned char lds_byte;
 constexpr int kRowsPerWave = 32;
 constexpr int kKPitch = kHeadDim * 2 + 16;  // bytes per K row in LDS (row-major)
 constexpr int kVPitch = kHeadDim * 2 + 64;  // bytes per V row in LDS (row-major, read transposed)
 constexpr float kLazyLog2 = 8.0f;           // the lazy reference max moves when a row grows by > 2^8
+// Keys per tile: 128 for the 8-wave workgroup (one per CU, LDS for two 74 KB
+// tile pairs), 64 for 4 waves (two workgroups per CU).  A tile never straddles
+// a 256-token block.
+template <int NW>
+constexpr int kTileKeys = NW == 8 ? 128 : 64;
+// Left by the fast pass in the first output element of a wave whose rows need
+// the exact pass: a signalling-NaN pattern, which no arithmetic result converted
+// to bf16 can have (those NaNs are quiet).
+constexpr uint16_t kFixupMarker = 0x7F81;
 }  // namespace
 
-// NW waves per workgroup (4 or 8); two waves per SIMD either way (two
-// workgroups of 4 per CU, or one of 8).
-template <int GW, bool PAGED, int NW>
-__global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a, int32_t m_blocks, int32_t n_work,
-                                                                  int32_t head_groups, int32_t chunk) {
+// Highest call number (see launch_attn_prefill) whose fast pass flagged a work
+// item; raised with a device-scope atomic, never lowered.  The exact pass of a
+// call scans for markers only when this is at least its own number.
+__device__ unsigned long long g_prefill_flagged_call = 0;
+
+namespace {
+}  // namespace
+
+// One work item: query block mb of (sequence b, kv head g, head group hg), with
+// NW waves (4 or 8; two waves per SIMD either way: two workgroups of 4 per CU,
+// or one of 8).  kExact selects the pass (see the tile loop below).  k_lds3 /
+// v_lds3 are the workgroup's tile buffers.
+template <int GW, bool PAGED, int NW, bool kExact>
+__device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_blocks, int32_t head_groups,
+                                              int32_t work, lds_byte* k_lds3, lds_byte* v_lds3, uint64_t call) {
     constexpr int kThreads = 64 * NW;
-    // Keys per tile: 128 for the 8-wave workgroup (one per CU, LDS for two 74 KB
-    // tile pairs), 64 for 4 waves (two workgroups per CU).  A tile never
-    // straddles a 256-token block.
-    constexpr int kKT = NW == 8 ? 128 : 64;
+    constexpr int kKT = kTileKeys<NW>;
     constexpr int kKH = kKT / 32;                       // 32-key blocks per tile
     constexpr int kKTileBytes = kKT * kKPitch;
     constexpr int kVTileBytes = kKT * kVPitch;
@@ -73,18 +102,9 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a,
     constexpr int kLoadIters = kKT / kLoadRows;         // sweeps per tile
     constexpr int kPosSub = NW / GW;                    // position sub-blocks per workgroup
     constexpr int kBM = kRowsPerWave * kPosSub;         // query positions per workgroup
-    __shared__ __attribute__((aligned(16))) unsigned char k_lds[2 * kKTileBytes];
-    __shared__ __attribute__((aligned(16))) unsigned char v_lds[2 * kVTileBytes];
+    unsigned char* k_lds = (unsigned char*)k_lds3;
+    unsigned char* v_lds = (unsigned char*)v_lds3;
 
-    // Chunks of `chunk` consecutive work items are dealt round-robin over the 8
-    // XCDs, which take workgroups round-robin by id: XCD x runs chunks x, x+8,
-    // x+16, ... in order.  A chunk is one (sequence, kv head, head group) unit --
-    // all its query blocks, so its K/V stays in one L2 -- unless there are fewer
-    // units than XCDs; then it is two query blocks, so few sequences still spread
-    // over all XCDs.
-    const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
-    const int work = (xcd + 8 * (kx / chunk)) * chunk + kx % chunk;
-    if (work >= n_work) return;
     // work = ((b * hkv + g) * head_groups + hg) * m_blocks + (m_blocks - 1 - mb)
     const int mb = m_blocks - 1 - (work % m_blocks);
     int rest = work / m_blocks;
@@ -100,9 +120,21 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a,
     if (p0 >= Lq || Lk < Lq || Lq <= 0) return;
     if (cq0 < 0 || cq1 > a.total_q || ck0 < 0) return;   // metadata outside the q/o rows: nothing is touched
     const int off = Lk - Lq;                            // absolute position of query 0
+    const int G = a.hq / a.hkv;
+    if (kExact) {
+        // Recompute this work item only if one of its waves left the marker.
+        bool flagged = false;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const int row = p0 + kRowsPerWave * (w / GW);
+            const int hd = g * G + hg * GW + (w % GW);
+            if (row < Lq)
+                flagged |= *((const uint16_t*)a.o + ((int64_t)(cq0 + row) * a.hq + hd) * kHeadDim) == kFixupMarker;
+        }
+        if (!flagged) return;
+    }
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int G = a.hq / a.hkv;
     const int head = g * G + hg * GW + (wave % GW);
     const int wp0 = p0 + kRowsPerWave * (wave / GW);    // first query (sequence-relative) of this wave
     const int wq_last = min(wp0 + kRowsPerWave, Lq) - 1;
@@ -115,39 +147,39 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a,
     const int wave_tiles = (wave_keys + kKT - 1) / kKT;
 
     // ---- Q^T as the B operand: lane owns query row l%32, dims 8*(l/32) + 16*st .. +7.
+    // For the fast pass Q is multiplied by softmax_scale * log2(e) once here (fp32,
+    // rounded back to bf16), so its products are scores in base-2 exponent units.
     const int qi = wp0 + (lane & 31);
     const int q_row = cq0 + min(qi, Lq - 1);
+    const uint16_t* qp = (const uint16_t*)a.q + (int64_t)min(q_row, a.total_q - 1) * a.q_row_stride +
+                         (int64_t)head * kHeadDim + 8 * (lane >> 5);
     bf16x8 qreg[8];
-    {
-        const uint16_t* qp = (const uint16_t*)a.q + (int64_t)min(q_row, a.total_q - 1) * a.q_row_stride +
-                             (int64_t)head * kHeadDim + 8 * (lane >> 5);
 #pragma unroll
-        for (int st = 0; st < 8; ++st) qreg[st] = __builtin_bit_cast(bf16x8, ldg128(qp + 16 * st));
+    for (int st = 0; st < 8; ++st) {
+        u32x4 w = ldg128(qp + 16 * st);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(bf16lo(w[e]) * a.scale_log2, bf16hi(w[e]) * a.scale_log2);
+        qreg[st] = __builtin_bit_cast(bf16x8, w);
     }
     const int qpos = off + qi;                          // absolute position of this lane's query
-
-    f32x16 oacc[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-    float m_run = -INFINITY, l_part = 0.f;      // running reference max (raw units), partial sum
-    const float lazy_raw = kLazyLog2 / a.scale_log2;
 
     // ---- tile loader.  Thread tid moves 16-byte piece tid%16 of rows tid/16 + kLoadRows*i
     // (i < kLoadIters) of the K and V tiles.  Row offsets are loop-invariant; every
     // load is issued on every path (rows past the last key are clamped onto it), so
     // the compiler's wait counts stay exact.
+    // Row strides are at most 2^24 elements (checked by the caller), so offsets
+    // inside one tile fit in 32 bits: a per-tile base plus a 32-bit lane offset.
     const int64_t krs = a.k_row_stride, vrs = a.v_row_stride;
+    const int32_t krs32 = (int32_t)krs, vrs32 = (int32_t)vrs;
     const uint16_t* kbase = (const uint16_t*)a.k + (int64_t)g * kHeadDim;
     const uint16_t* vbase = (const uint16_t*)a.v + (int64_t)g * kHeadDim;
     const int32_t* bt = PAGED ? a.block_table + (int64_t)b * a.max_blocks : nullptr;
     const int lrow = tid >> 4, piece = tid & 15;
-    int64_t koff[kLoadIters], voff[kLoadIters];
+    int32_t koff[kLoadIters], voff[kLoadIters];
 #pragma unroll
     for (int i = 0; i < kLoadIters; ++i) {
-        koff[i] = (int64_t)(lrow + kLoadRows * i) * krs + piece * 8;
-        voff[i] = (int64_t)(lrow + kLoadRows * i) * vrs + piece * 8;
+        koff[i] = (lrow + kLoadRows * i) * krs32 + piece * 8;
+        voff[i] = (lrow + kLoadRows * i) * vrs32 + piece * 8;
     }
     // First cache/array row of tile t and whether its block id is usable (tiles
     // never straddle a 256-token block).
@@ -168,9 +200,9 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a,
         bool ok;
         const int64_t r0 = tile_row0(t, ok);
         const int last = Lk - 1 - t * kKT;              // last valid row of this tile (>= 0)
+        const uint16_t* kp = kbase + r0 * krs;
+        const uint16_t* vp = vbase + r0 * vrs;
         if (ok && last >= kKT - 1) {
-            const uint16_t* kp = kbase + r0 * krs;
-            const uint16_t* vp = vbase + r0 * vrs;
 #pragma unroll
             for (int i = 0; i < kLoadIters; ++i) kst[i] = ldg128(kp + koff[i]);
 #pragma unroll
@@ -179,13 +211,13 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a,
             // partial or unusable tile: clamp rows onto valid memory, zero V at store time
 #pragma unroll
             for (int i = 0; i < kLoadIters; ++i) {
-                const int64_t row = r0 + (ok ? min(lrow + kLoadRows * i, last) : 0);
-                kst[i] = ldg128(kbase + row * krs + piece * 8);
+                const int row = ok ? min(lrow + kLoadRows * i, last) : 0;
+                kst[i] = ldg128(kp + (row * krs32 + piece * 8));
             }
 #pragma unroll
             for (int i = 0; i < kLoadIters; ++i) {
-                const int64_t row = r0 + (ok ? min(lrow + kLoadRows * i, last) : 0);
-                vst[i] = ldg128(vbase + row * vrs + piece * 8);
+                const int row = ok ? min(lrow + kLoadRows * i, last) : 0;
+                vst[i] = ldg128(vp + (row * vrs32 + piece * 8));
             }
         }
     };
@@ -208,115 +240,181 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a,
     };
 
     const int h32 = lane >> 5;  // which half of the k-slots this lane feeds
-    // Double-buffered LDS tiles: one barrier per tile.  Tile t is computed from buffer
-    // t&1 while tile t+1 (loaded into registers one iteration earlier) is stored into
-    // the other buffer; tile t+2 is loaded after the barrier.
-    load_tile(0);
-    store_tile(0, k_lds, v_lds);
-    if (1 < n_tiles) load_tile(1);
-    __syncthreads();
-    for (int t = 0; t < n_tiles; ++t) {
-        unsigned char* kb = k_lds + (t & 1) * kKTileBytes;
-        unsigned char* vb = v_lds + (t & 1) * kVTileBytes;
-        if (t < wave_tiles) {   // this wave still has visible keys in tile t
-          const int j0 = t * kKT;
-        bool ok;
-        (void)tile_row0(t, ok);
-        // ---- S^T = K Q^T for the tile's 32-key blocks
-        // The key blocks are independent accumulation chains; interleaving them
-        // keeps consecutive MFMAs independent so each issues without waiting for the
-        // previous result.
-        f32x16 s[kKH];
-#pragma unroll
-        for (int kh = 0; kh < kKH; ++kh)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[kh][r] = 0.f;
-#pragma unroll
-        for (int st = 0; st < 8; ++st)
-#pragma unroll
-            for (int kh = 0; kh < kKH; ++kh) {
-                const unsigned char* kr = kb + (32 * kh + (lane & 31)) * kKPitch + 16 * h32;
-                const bf16x8 av = *reinterpret_cast<const bf16x8*>(kr + 32 * st);
-                s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[st], s[kh], 0, 0, 0);
-            }
-        // s[kh][r] = raw score of key j0 + 32kh + 8(r/4) + 4*h32 + r%4 for query qi.
-        const bool need_mask = !ok || (j0 + kKT - 1 > off + wp0) || (j0 + kKT > Lk);
-        if (need_mask) {
-            // key j0 + 4*h32 + c (c a compile-time offset) is visible iff c <= lim
-            const int lim = ok ? min(qpos, Lk - 1) - (j0 + 4 * h32) : -1;
-#pragma unroll
-            for (int kh = 0; kh < kKH; ++kh)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int c = 32 * kh + 8 * (r >> 2) + (r & 3);
-                    s[kh][r] = c > lim ? -INFINITY : s[kh][r];
-                }
-        }
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int kh = 0; kh < kKH; ++kh)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) tmax = __builtin_fmaxf(__builtin_fmaxf(tmax, s[kh][r]), s[kh][r + 1]);
-        {
-            // exchange with the lane 32 away without an LDS round trip (v_permlane32_swap)
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-            tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        // Lazy reference max (raw score units): it moves only when a row's max grows
-        // by more than 2^kLazyLog2 in the exponent, so the weights stay <= 256 and the
-        // O rescale is skipped on most tiles.  Exact: O and l share the reference.
-        const bool grow = tmax > m_run + lazy_raw;
-        if (__any(grow)) {
-            const float mn = grow ? tmax : m_run;
-            const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - mn) * a.scale_log2);
-            m_run = mn;
-            l_part *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-        }
-        const float moff = m_run == -INFINITY ? 0.f : -m_run * a.scale_log2;
-        float psum = 0.f;
-        uint32_t pk[kKH][8];
-#pragma unroll
-        for (int kh = 0; kh < kKH; ++kh)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kh][r], a.scale_log2, moff));
-                const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kh][r + 1], a.scale_log2, moff));
-                psum += e0 + e1;
-                pk[kh][r >> 1] = pack_bf16x2(e0, e1);
-            }
-        l_part += psum;
 
-        // ---- O^T += V^T P^T: per 16-key step (kh, v) the B operand is registers 8v..8v+7 of s[kh].
-        // The A operand (V^T: row d = lane%32, 8 keys) comes from row-major V with two
-        // transposing LDS reads: lane j of a 16-lane group addresses key j/4, dims 4*(j%4)
-        // of a 4-key x 16-dim tile and receives its own dim across the 4 keys.
-        const int grp16 = lane >> 4, j16 = lane & 15;
+    f32x16 oacc[4];
+    float m_run, l_part;                  // reference max (raw score units) and partial row sum
+    const float lazy_raw = kLazyLog2 / a.scale_log2;
+
+    // One pass over the key tiles.  Double-buffered LDS tiles: one barrier per tile.
+    // Tile t is computed from buffer t&1 while tile t+1 (loaded into registers one
+    // iteration earlier) is stored into the other buffer; tile t+2 is loaded after
+    // the barrier.
+    //   Fast pass (kExact false): Q pre-scaled, the weights are exp2(score) against
+    //   a fixed reference of 0 -- no row max, no rescale, one VALU op less per score.
+    //   Softmax does not depend on the reference and floating point is
+    //   scale-invariant away from overflow and underflow, so this is the same
+    //   computation while a row's sum stays inside [2^-64, 2^64] and its O finite
+    //   (scores within about +-64 in base-2 units, where rounding the scaled Q to
+    //   bf16 moves a weight by less than bf16 rounding of P does); checked afterwards.
+    //   Exact pass (kExact true): Q as given, scale applied in fp32, and the online
+    //   softmax with a lazy reference max that moves only when a row grows by more
+    //   than 2^8, so the O rescale is skipped on most tiles.  Exact for any input:
+    //   O and l always share the reference.
+    {
+        constexpr int kSub = kExact && kKH > 1 ? 2 : 1;   // steps per tile
+        constexpr int kKHs = kKH / kSub;                   // 32-key blocks per step
 #pragma unroll
-        for (int kh = 0; kh < kKH; ++kh)
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int v = 0; v < 2; ++v) {
-                u32x4 bw = {pk[kh][4 * v], pk[kh][4 * v + 1], pk[kh][4 * v + 2], pk[kh][4 * v + 3]};
-                const bf16x8 bv = __builtin_bit_cast(bf16x8, bw);
-                const int kcol = 32 * kh + 16 * v + 4 * h32;   // first key of this lane's k-slots
+            for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+        m_run = -INFINITY;
+        l_part = 0.f;
+        if (kExact) {
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    const int d0 = 32 * dt + 16 * (grp16 & 1) + 4 * (j16 & 3);
-                    lds_ptr_t p0 = (lds_ptr_t)(vb + (kcol + (j16 >> 2)) * kVPitch + 2 * d0);
-                    lds_ptr_t p1 = (lds_ptr_t)(vb + (kcol + 8 + (j16 >> 2)) * kVPitch + 2 * d0);
-                    const bf16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p0);
-                    const bf16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p1);
-                    const bf16x8 av = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, oacc[dt], 0, 0, 0);
+            for (int st = 0; st < 8; ++st) qreg[st] = __builtin_bit_cast(bf16x8, ldg128(qp + 16 * st));
+        }
+        load_tile(0);
+        store_tile(0, k_lds, v_lds);
+        if (1 < n_tiles) load_tile(1);
+        __syncthreads();
+        for (int t = 0; t < n_tiles; ++t) {
+            unsigned char* kb = k_lds + (t & 1) * kKTileBytes;
+            unsigned char* vb = v_lds + (t & 1) * kVTileBytes;
+            if (t < wave_tiles) {   // this wave still has visible keys in tile t
+                const int j0 = t * kKT;
+                bool ok;
+                (void)tile_row0(t, ok);
+                // The fast pass takes the tile in one step; the exact pass in kSub steps of
+                // kKHs 32-key blocks, which holds fewer scores in registers at a time.
+                for (int sub = 0; sub < kSub; ++sub) {
+                    const int kb0 = sub * kKHs;   // first 32-key block of this step
+                    // ---- S^T = K Q^T for the tile's 32-key blocks
+                    // The key blocks are independent accumulation chains; interleaving them
+                    // keeps consecutive MFMAs independent so each issues without waiting for the
+                    // previous result.
+                    f32x16 s[kKHs];
+#pragma unroll
+                    for (int kh = 0; kh < kKHs; ++kh)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) s[kh][r] = 0.f;
+#pragma unroll
+                    for (int st = 0; st < 8; ++st)
+#pragma unroll
+                        for (int kh = 0; kh < kKHs; ++kh) {
+                            const unsigned char* kr = kb + (32 * (kb0 + kh) + (lane & 31)) * kKPitch + 16 * h32;
+                            const bf16x8 av = *reinterpret_cast<const bf16x8*>(kr + 32 * st);
+                            s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[st], s[kh], 0, 0, 0);
+                        }
+                    // s[kh][r] = score of key j0 + 32(kb0+kh) + 8(r/4) + 4*h32 + r%4 for query qi
+                    // (base-2 units in the fast pass, raw in the exact pass).
+                    const int jend = j0 + 32 * (kb0 + kKHs);        // one past the step's last key
+                    const bool need_mask = !ok || (jend - 1 > off + wp0) || (jend > Lk);
+                    if (need_mask) {
+                        // key j0 + 4*h32 + c (c a compile-time offset) is visible iff c <= lim
+                        const int lim = ok ? min(qpos, Lk - 1) - (j0 + 4 * h32) : -1;
+#pragma unroll
+                        for (int kh = 0; kh < kKHs; ++kh)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int c = 32 * (kb0 + kh) + 8 * (r >> 2) + (r & 3);
+                                s[kh][r] = c > lim ? -INFINITY : s[kh][r];
+                            }
+                    }
+                    float moff = 0.f;
+                    if (kExact) {
+                        float tmax = -INFINITY;
+#pragma unroll
+                        for (int kh = 0; kh < kKHs; ++kh)
+#pragma unroll
+                            for (int r = 0; r < 16; r += 2)
+                                tmax = __builtin_fmaxf(__builtin_fmaxf(tmax, s[kh][r]), s[kh][r + 1]);
+                        {
+                            // exchange with the lane 32 away without an LDS round trip (v_permlane32_swap)
+                            const uint32_t tb = __float_as_uint(tmax);
+                            const auto sw = __builtin_amdgcn_permlane32_swap(tb, tb, false, false);
+                            tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+                        }
+                        const bool grow = tmax > m_run + lazy_raw;
+                        if (__any(grow)) {
+                            const float mn = grow ? tmax : m_run;
+                            const float alpha =
+                                m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - mn) * a.scale_log2);
+                            m_run = mn;
+                            l_part *= alpha;
+#pragma unroll
+                            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+                        }
+                        moff = m_run == -INFINITY ? 0.f : -m_run * a.scale_log2;
+                    }
+                    float psum = 0.f;
+                    uint32_t pk[kKHs][8];
+#pragma unroll
+                    for (int kh = 0; kh < kKHs; ++kh)
+#pragma unroll
+                        for (int r = 0; r < 16; r += 2) {
+                            const float x0 = kExact ? fmaf(s[kh][r], a.scale_log2, moff) : s[kh][r];
+                            const float x1 = kExact ? fmaf(s[kh][r + 1], a.scale_log2, moff) : s[kh][r + 1];
+                            const float e0 = __builtin_amdgcn_exp2f(x0);
+                            const float e1 = __builtin_amdgcn_exp2f(x1);
+                            psum += e0 + e1;
+                            pk[kh][r >> 1] = pack_bf16x2(e0, e1);
+                        }
+                    l_part += psum;
+
+                    // ---- O^T += V^T P^T: per 16-key step (kh, v) the B operand is registers 8v..8v+7 of s[kh].
+                    // The A operand (V^T: row d = lane%32, 8 keys) comes from row-major V with two
+                    // transposing LDS reads: lane j of a 16-lane group addresses key j/4, dims 4*(j%4)
+                    // of a 4-key x 16-dim tile and receives its own dim across the 4 keys.
+                    const int grp16 = lane >> 4, j16 = lane & 15;
+#pragma unroll
+                    for (int kh = 0; kh < kKHs; ++kh)
+#pragma unroll
+                        for (int v = 0; v < 2; ++v) {
+                            u32x4 bw = {pk[kh][4 * v], pk[kh][4 * v + 1], pk[kh][4 * v + 2], pk[kh][4 * v + 3]};
+                            const bf16x8 bv = __builtin_bit_cast(bf16x8, bw);
+                            const int kcol = 32 * (kb0 + kh) + 16 * v + 4 * h32;   // first key of this lane's k-slots
+#pragma unroll
+                            for (int dt = 0; dt < 4; ++dt) {
+                                const int d0 = 32 * dt + 16 * (grp16 & 1) + 4 * (j16 & 3);
+                                lds_ptr_t p0 = (lds_ptr_t)(vb + (kcol + (j16 >> 2)) * kVPitch + 2 * d0);
+                                lds_ptr_t p1 = (lds_ptr_t)(vb + (kcol + 8 + (j16 >> 2)) * kVPitch + 2 * d0);
+                                const bf16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p0);
+                                const bf16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p1);
+                                const bf16x8 av = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+                                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, oacc[dt], 0, 0, 0);
+                            }
+                        }
                 }
             }
+            if (t + 1 < n_tiles)
+                store_tile(t + 1, k_lds + ((t + 1) & 1) * kKTileBytes, v_lds + ((t + 1) & 1) * kVTileBytes);
+            __syncthreads();
+            if (t + 2 < n_tiles) load_tile(t + 2);
         }
-        if (t + 1 < n_tiles) store_tile(t + 1, k_lds + ((t + 1) & 1) * kKTileBytes, v_lds + ((t + 1) & 1) * kVTileBytes);
-        __syncthreads();
-        if (t + 2 < n_tiles) load_tile(t + 2);
+    }
+
+    if (!kExact) {
+        // Did every live row of this wave stay inside the fast pass's range?  l in
+        // [2^-64, 2^64] bounds every weight and keeps the row clear of underflow; a
+        // finite sum of this lane's O entries means no product overflowed.  If not,
+        // the wave leaves kFixupMarker in its first output element instead of its
+        // results, and the exact pass recomputes the whole work item.
+        const float l_fast = l_part + __shfl_xor(l_part, 32, 64);
+        float osum = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) osum += oacc[dt][r];
+        const bool row_bad = wave_live && !(l_fast >= 0x1p-64f && l_fast <= 0x1p64f && osum - osum == 0.f);
+        if (__any(row_bad)) {
+            if (lane == 0) {
+                *((uint16_t*)a.o + ((int64_t)(cq0 + wp0) * a.hq + head) * kHeadDim) = kFixupMarker;
+                atomicMax(&g_prefill_flagged_call, (unsigned long long)call);
+            }
+            return;
+        }
     }
 
     // ---- normalise and store: lane holds O^T[d][qi] for d = 32dt + 8(r/4) + 4*h32 + r%4.
@@ -336,6 +434,43 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a,
             w[1] = pack_bf16x2(oacc[dt][4 * r4 + 2] * inv, oacc[dt][4 * r4 + 3] * inv);
             *reinterpret_cast<u32x2*>(op + d) = w;
         }
+}
+
+// The two passes are separate kernels so that the exact pass's code does not
+// change how the compiler schedules the fast pass's loop.  The launcher runs the
+// fast pass, then the exact pass as a persistent kernel of at most one
+// workgroup per CU slot, which exits at once unless this call flagged something.
+template <int GW, bool PAGED, int NW>
+__global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a, int32_t m_blocks, int32_t n_work,
+                                                                  int32_t head_groups, int32_t chunk, uint64_t call) {
+    constexpr int kKT = kTileKeys<NW>;
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds[2 * kKT * kKPitch];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds[2 * kKT * kVPitch];
+
+    // Chunks of `chunk` consecutive work items are dealt round-robin over the 8
+    // XCDs, which take workgroups round-robin by id: XCD x runs chunks x, x+8,
+    // x+16, ... in order.  A chunk is one (sequence, kv head, head group) unit --
+    // all its query blocks, so its K/V stays in one L2 -- unless there are fewer
+    // units than XCDs; then it is two query blocks, so few sequences still spread
+    // over all XCDs.
+    const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
+    const int work = (xcd + 8 * (kx / chunk)) * chunk + kx % chunk;
+    if (work >= n_work) return;
+    prefill_block<GW, PAGED, NW, false>(a, m_blocks, head_groups, work, (lds_byte*)k_lds, (lds_byte*)v_lds, call);
+}
+
+template <int GW, bool PAGED, int NW>
+__global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_exact_kernel(PrefillArgs a, int32_t m_blocks,
+                                                                        int32_t n_work, int32_t head_groups,
+                                                                        uint64_t call) {
+    constexpr int kKT = kTileKeys<NW>;
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds[2 * kKT * kKPitch];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds[2 * kKT * kVPitch];
+    if (__hip_atomic_load(&g_prefill_flagged_call, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < call) return;
+    // Every workgroup walks the same item sequence, so the barriers inside match;
+    // each item returns at once unless one of its waves left the marker.
+    for (int work = blockIdx.x; work < n_work; work += gridDim.x)
+        prefill_block<GW, PAGED, NW, true>(a, m_blocks, head_groups, work, (lds_byte*)k_lds, (lds_byte*)v_lds, call);
 }
 
 hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t stream) {
@@ -363,10 +498,20 @@ hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t stream) {
     const int64_t grid64 = ((n_chunks + 7) / 8) * 8 * chunk;
     if (grid64 > (int64_t)0x7FFFFFF0) return hipErrorInvalidValue;
     const int grid = (int)grid64;
+    // Exact pass: one workgroup per CU slot (two 4-wave or one 8-wave per CU).
+    const int grid_exact = (int)std::min<int64_t>(n_work64, nw == 8 ? 256 : 512);
+    // Each call gets a number of its own, so the exact pass can tell whether this
+    // call's fast pass flagged anything (the device keeps the highest number seen).
+    static std::atomic<uint64_t> s_calls{0};
+    const uint64_t call = s_calls.fetch_add(1, std::memory_order_relaxed) + 1;
     const bool paged = a.block_table != nullptr;
 #define PKV_PREFILL(GW_, PG_, NW_)                                                                               \
-    hipLaunchKernelGGL((prefill_kernel<GW_, PG_, NW_>), dim3(grid), dim3(64 * NW_), 0, stream, a, m_blocks, n_work, \
-                       head_groups, (int32_t)chunk)
+    do {                                                                                                         \
+        hipLaunchKernelGGL((prefill_kernel<GW_, PG_, NW_>), dim3(grid), dim3(64 * NW_), 0, stream, a, m_blocks,  \
+                           n_work, head_groups, (int32_t)chunk, call);                                           \
+        hipLaunchKernelGGL((prefill_exact_kernel<GW_, PG_, NW_>), dim3(grid_exact), dim3(64 * NW_), 0, stream,   \
+                           a, m_blocks, n_work, head_groups, call);                                              \
+    } while (0)
     if (gw == 4) {
         if (wide) {
             if (paged) PKV_PREFILL(4, true, 8); else PKV_PREFILL(4, false, 8);

@@ -80,7 +80,8 @@ def test_store_kvcache_validation(lib):
 
 def test_prefill_validation(lib):
     f = lib.pkv_attn_prefill_varlen
-    base = [FAKE, 4096, FAKE, 4096, FAKE, 4096, FAKE, FAKE, FAKE, 2, 337, 300, 300, 16, 8, 128, 0.088, 1, None, 0,
+    o_fake = FAKE.value + (1 << 32)          # an output buffer away from q
+    base = [FAKE, 4096, FAKE, 4096, FAKE, 4096, o_fake, FAKE, FAKE, 2, 337, 300, 300, 16, 8, 128, 0.088, 1, None, 0,
             256, 0, None]
     a = list(base); a[17] = 0                # causal = 0 is not built
     assert f(*a) == -2
@@ -92,6 +93,12 @@ def test_prefill_validation(lib):
     assert f(*a) == -1 and "caches" in _err(lib)
     a = list(base); a[18] = FAKE; a[3] = a[5] = 1024; a[19] = 2; a[20] = 128; a[21] = 8   # block size 128
     assert f(*a) == -2
+    a = list(base); a[3] = (1 << 24) + 8      # k row stride beyond 2^24 elements
+    assert f(*a) == -1 and "2^24" in _err(lib)
+    a = list(base); a[6] = FAKE.value + 4096 * 2 * 336   # o starting inside q's last row
+    assert f(*a) == -1 and "overlap" in _err(lib)
+    a = list(base); a[0] = 1 << 34; a[6] = (1 << 34) - 337 * 16 * 128 * 2 + 16   # o ending 8 elements into q
+    assert f(*a) == -1 and "overlap" in _err(lib)
     a = list(base); a[9] = 0                 # no sequences: no-op
     assert f(*a) == 0
 

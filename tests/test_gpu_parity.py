@@ -178,13 +178,16 @@ def test_store_kvcache_skips_out_of_range_slots(dev):
 # prefill
 # ---------------------------------------------------------------------------
 
-def _prefill_case(dev, lens_q, lens_k, hq, hkv, seed, paged=False, num_blocks=None, rows=None):
+def _prefill_case(dev, lens_q, lens_k, hq, hkv, seed, paged=False, num_blocks=None, rows=None, make_qkv=None):
     rng = wl.rng_for(92, seed, 0)
     cuq, cuk = wl.cu_seqlens(lens_q), wl.cu_seqlens(lens_k)
     tq, tk = int(cuq[-1]), int(cuk[-1])
-    q = wl.normal_bf16(rng, (tq, hq, D))
-    k = wl.normal_bf16(rng, (tk, hkv, D))
-    v = wl.normal_bf16(rng, (tk, hkv, D))
+    if make_qkv is None:
+        q = wl.normal_bf16(rng, (tq, hq, D))
+        k = wl.normal_bf16(rng, (tk, hkv, D))
+        v = wl.normal_bf16(rng, (tk, hkv, D))
+    else:
+        q, k, v = make_qkv(rng, tq, tk)
     if not paged:
         o = pkv.attn_prefill_varlen(to_dev(q, dev), to_dev(k, dev), to_dev(v, dev), to_dev(cuq, dev),
                                     to_dev(cuk, dev), max(lens_q), max(lens_k))
@@ -244,6 +247,53 @@ def test_prefill_few_work_units(dev, lens, hq, hkv):
     check_attn(f64(o), ref, "prefill few units")
     o2, ref2, _ = _prefill_case(dev, [min(64, L) for L in lens], lens, hq, hkv, seed=sum(lens), paged=True)
     check_attn(f64(o2), ref2, "prefill few units, paged")
+
+
+def _extreme_scores(hq, hkv, kind):
+    """q, k, v makers whose scores leave the range of the kernel's fast pass for a few
+    query heads: 'large' scales those q rows by 40 (scores of several hundred in
+    base-2 units, weights past 2^64 against a zero reference); 'small' points those
+    q rows against a direction every key of kv head 0 shares (every score near -100
+    in base-2 units, weights below 2^-64).  Other heads keep ordinary scores, so
+    workgroups mixing both kinds of rows are exercised too."""
+    G = hq // hkv
+
+    def make(rng, tq, tk):
+        q = wl.bf16_to_f32(wl.normal_bf16(rng, (tq, hq, D))).astype(np.float64)
+        k = wl.bf16_to_f32(wl.normal_bf16(rng, (tk, hkv, D))).astype(np.float64)
+        v = wl.normal_bf16(rng, (tk, hkv, D))
+        if kind == "large":
+            q[:, 0] *= 40.0
+            q[:, hq - 1] *= 40.0
+        else:
+            u = rng.choice([-1.0, 1.0], size=D)
+            k[:, 0] = u + 0.05 * k[:, 0]
+            q[:, :G] = -6.0 * u + 0.5 * q[:, :G]
+        return wl.bf16_bits(q), wl.bf16_bits(k), v
+    return make
+
+
+@pytest.mark.parametrize("kind", ["large", "small"])
+@pytest.mark.parametrize("lens_q,lens_k,hq,hkv,paged", [([300, 700, 45], [300, 700, 45], 16, 8, False),
+                                                         ([2048, 2100], [2048, 2100], 32, 8, False),
+                                                         ([2048, 2100], [2100, 2300], 32, 8, True),
+                                                         ([64, 257], [600, 300], 8, 8, True),
+                                                         ([200] * 40, [200] * 40, 32, 8, False)])
+def test_prefill_scores_outside_fast_range(dev, kind, lens_q, lens_k, hq, hkv, paged):
+    """Rows whose softmax sum leaves [2^-64, 2^64] against a zero reference are
+    recomputed with the running-max pass; results match the oracle either way.
+    The last case has more work items (2240) than the exact pass has workgroups,
+    so its workgroups walk several items each."""
+    _say(f"prefill, {kind} scores on some heads, Lq {lens_q} Lk {lens_k}, {hq}/{hkv} heads, paged={paged}")
+    T = sum(lens_q)
+    t = np.arange(0, T, 3)
+    rows = np.concatenate([np.stack([t, np.zeros_like(t)], 1), np.stack([t, np.full_like(t, hq - 1)], 1),
+                           np.stack([t, (t // 3) % hq], 1)])
+    o, ref, _ = _prefill_case(dev, lens_q, lens_k, hq, hkv, seed=7 + hq, paged=paged, rows=rows,
+                              make_qkv=_extreme_scores(hq, hkv, kind))
+    got = f64(o)[rows[:, 0], rows[:, 1]]
+    assert np.isfinite(got).all()
+    check_attn(got, ref, f"prefill {kind} scores")
 
 
 def test_prefill_paged_prefix(dev):
