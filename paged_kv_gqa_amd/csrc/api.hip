@@ -240,6 +240,7 @@ int pkv_attn_prefill_varlen(const void* q, int64_t q_row_stride, const void* k, 
     a.num_seqs = num_seqs;
     a.total_q = total_q;
     a.max_seqlen_q = max_seqlen_q;
+    a.max_seqlen_k = max_seqlen_k;
     a.hq = num_q_heads;
     a.hkv = num_kv_heads;
     a.scale_log2 = softmax_scale * 1.4426950408889634f;

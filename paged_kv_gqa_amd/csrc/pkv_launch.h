@@ -56,6 +56,7 @@ struct PrefillArgs {
     int32_t num_seqs;
     int32_t total_q;
     int32_t max_seqlen_q;
+    int32_t max_seqlen_k;
     int32_t hq;
     int32_t hkv;
     float scale_log2;            // softmax_scale * log2(e)

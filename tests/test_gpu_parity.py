@@ -274,21 +274,26 @@ def _extreme_scores(hq, hkv, kind):
 
 
 @pytest.mark.parametrize("kind", ["large", "small"])
-@pytest.mark.parametrize("lens_q,lens_k,hq,hkv,paged", [([300, 700, 45], [300, 700, 45], 16, 8, False),
-                                                         ([2048, 2100], [2048, 2100], 32, 8, False),
-                                                         ([2048, 2100], [2100, 2300], 32, 8, True),
-                                                         ([64, 257], [600, 300], 8, 8, True),
-                                                         ([200] * 40, [200] * 40, 32, 8, False)])
-def test_prefill_scores_outside_fast_range(dev, kind, lens_q, lens_k, hq, hkv, paged):
+@pytest.mark.parametrize("lens_q,lens_k,hq,hkv,paged,step", [
+    ([300, 700, 45], [300, 700, 45], 16, 8, False, 3),                  # exact pass alone, 4 waves
+    ([2048, 2100], [2100, 2300], 32, 8, True, 3),                       # exact pass alone, 8 waves
+    ([4096, 4096], [4096, 4096], 32, 8, False, 7),                      # two passes, 8 waves, G = 4
+    ([1024] * 40, [1024] * 40, 16, 8, False, 29),                       # two passes, 4 waves, G = 2
+    ([1000] * 8, [8000] * 8, 8, 8, True, 7),                            # two passes, 4 waves, G = 1, paged
+    ([1024] * 32, [1024] * 32, 32, 8, False, 23)])                      # two passes, 8192 work items
+def test_prefill_scores_outside_fast_range(dev, kind, lens_q, lens_k, hq, hkv, paged, step):
     """Rows whose softmax sum leaves [2^-64, 2^64] against a zero reference are
     recomputed with the running-max pass; results match the oracle either way.
-    The last case has more work items (2240) than the exact pass has workgroups,
-    so its workgroups walk several items each."""
-    _say(f"prefill, {kind} scores on some heads, Lq {lens_q} Lk {lens_k}, {hq}/{hkv} heads, paged={paged}")
+    The first two batches are small enough to run the exact pass alone (one
+    launch); the others run both passes, with GQA groups of 4, 2 and 1, and (last
+    case) far more work items than the exact pass has workgroups, so each of its
+    workgroups walks several items."""
+    _say(f"prefill, {kind} scores on some heads, Lq {lens_q[:3]}.. Lk {lens_k[:3]}.. ({len(lens_q)} seqs), "
+         f"{hq}/{hkv} heads, paged={paged}")
     T = sum(lens_q)
-    t = np.arange(0, T, 3)
+    t = np.arange(0, T, step)
     rows = np.concatenate([np.stack([t, np.zeros_like(t)], 1), np.stack([t, np.full_like(t, hq - 1)], 1),
-                           np.stack([t, (t // 3) % hq], 1)])
+                           np.stack([t, (t // step) % hq], 1)])
     o, ref, _ = _prefill_case(dev, lens_q, lens_k, hq, hkv, seed=7 + hq, paged=paged, rows=rows,
                               make_qkv=_extreme_scores(hq, hkv, kind))
     got = f64(o)[rows[:, 0], rows[:, 1]]
