@@ -23,18 +23,20 @@
 //     long sequences (mean query length >= 2048) the workgroup has 8 waves
 //     (4 heads x 64 positions, or 2 x 128) and 128-key tiles, so each K/V tile
 //     staged in LDS feeds 256 query rows; otherwise 4 waves and 64-key tiles
-//     (more, smaller workgroups).  K and V are both kept row-major in LDS
-//     (plain 16-byte copies, padded rows: no bank conflicts); the PV product
-//     needs V transposed, which the gfx950 transposing LDS read
+//     (more, smaller workgroups).  K and V are both kept row-major in LDS; the
+//     PV product needs V transposed, which the gfx950 transposing LDS read
 //     (ds_read_b64_tr_b16) delivers: lane j of a 16-lane group addresses key
 //     j/4, dims 4*(j%4) of a 4-key x 16-dim tile and receives its own dim
 //     across the 4 keys.
-//   * Double-buffered LDS (one barrier per tile); the tile after next is
-//     loaded into registers while the current one is computed.  Tiles (128
-//     keys with 8 waves, 64 with 4) never straddle a 256-token block, so the
-//     paged loader does one block-table lookup per tile.  Loads are issued on
-//     every path (rows past the last key are clamped) so the compiler's wait
-//     counts stay exact.
+//   * Double-buffered LDS, one barrier per tile.  Tiles (128 keys with 8
+//     waves, 64 with 4) never straddle a 256-token block, so the paged loader
+//     does one block-table lookup per tile.  The fast pass copies each tile
+//     straight from global memory into LDS (global_load_lds_dwordx4, issued
+//     right after the barrier for the next tile while this one is computed):
+//     no staging registers and no LDS store instructions; rows are unpadded
+//     with 16-byte slots XOR-swizzled per row so the operand reads stay
+//     conflict-free.  The exact pass stages tiles through registers into padded
+//     rows (16-byte copies; rows past the last key clamped, V zeroed there).
 //   * Softmax in two passes.  The fast pass (one kernel) pre-scales Q by
 //     softmax_scale * log2(e) and takes exp2 of each score against a fixed
 //     reference of 0: no row max, no rescale, three VALU operations per score
@@ -46,7 +48,7 @@
 //     items, with Q as given, the scale in fp32, and an online running max that
 //     moves only when a row grows by more than 2^8.  A call with nothing
 //     flagged costs one short launch whose workgroups read one word and exit;
-//     batches under 2.5e11 FLOP run the exact pass alone in one launch.
+//     batches under 2e10 FLOP run the exact pass alone in one launch.
 //   * Causal tile skipping: a wave stops at the tile holding its last visible
 //     key; only tiles that cross the diagonal (or the sequence end) are masked.
 //   * Work order: longest query blocks first inside each (sequence, kv head);
@@ -97,8 +99,14 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
     constexpr int kThreads = 64 * NW;
     constexpr int kKT = kTileKeys<NW>;
     constexpr int kKH = kKT / 32;                       // 32-key blocks per tile
-    constexpr int kKTileBytes = kKT * kKPitch;
-    constexpr int kVTileBytes = kKT * kVPitch;
+    // The fast pass copies tiles straight from global memory into LDS
+    // (global_load_lds_dwordx4: a wave-instruction fills 1 KB of consecutive LDS),
+    // so its rows are unpadded and XOR-swizzled in 16-byte slots instead.
+    constexpr bool kDma = !kExact;
+    constexpr int kKP = kDma ? kHeadDim * 2 : kKPitch;
+    constexpr int kVP = kDma ? kHeadDim * 2 : kVPitch;
+    constexpr int kKTileBytes = kKT * kKP;
+    constexpr int kVTileBytes = kKT * kVP;
     constexpr int kLoadRows = kThreads / 16;            // tile rows one sweep of 16-byte pieces covers
     constexpr int kLoadIters = kKT / kLoadRows;         // sweeps per tile
     constexpr int kPosSub = NW / GW;                    // position sub-blocks per workgroup
@@ -199,6 +207,29 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
             return (int64_t)ck0 + j0;
         }
     };
+    // Fast pass: block id of tile t (0 when K/V are contiguous), loaded one iteration
+    // before it is needed, and the tile's first row from it.
+    // The load takes a clamped index plus an opaque per-lane zero, so the compiler
+    // keeps the value in a vector register and does not wait for it until blk_of
+    // (next iteration, after the barrier's wait) moves it to a scalar and applies
+    // the table bound.
+    int32_t lane_zero;
+    asm("v_mov_b32 %0, 0" : "=v"(lane_zero));
+    auto load_blk = [&](int t) -> int32_t {
+        if (!PAGED) return 0;
+        return bt[min(t * kKT / kBlockSize, a.max_blocks - 1) + lane_zero];
+    };
+    auto blk_of = [&](int t, int32_t raw) -> int32_t {
+        return t * kKT / kBlockSize < a.max_blocks ? __builtin_amdgcn_readfirstlane(raw) : -1;
+    };
+    auto row0_of = [&](int t, int32_t blk, bool& ok) -> int64_t {
+        if (PAGED) {
+            ok = blk >= 0 && (int64_t)blk < a.num_blocks;
+            return ok ? (int64_t)blk * kBlockSize + (t * kKT) % kBlockSize : 0;
+        }
+        ok = true;
+        return (int64_t)ck0 + t * kKT;
+    };
     u32x4 kst[kLoadIters], vst[kLoadIters];
     auto load_tile = [&](int t) {
         bool ok;
@@ -242,6 +273,76 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
             *reinterpret_cast<u32x4*>(vb + (lrow + kLoadRows * i) * kVPitch + piece * 16) = vst[i];
         }
     };
+    // Direct copies (fast pass): wave w fills rows 4(w*kDmaPerWave + u) + lane/16,
+    // u < kDmaPerWave, of both tiles; lane l lands in slot l%16 of its row.  Slot s of
+    // K row r holds 16-byte piece s ^ (r % 16), of V row r piece s ^ 4(r % 4): the
+    // MFMA operand reads below then touch every bank once per group of lanes.
+    constexpr int kDmaPerWave = kKT / 4 / NW;
+    const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int drow = lane >> 4, dslot = lane & 15;
+    int32_t kdoff[kDmaPerWave], vdoff[kDmaPerWave];
+#pragma unroll
+    for (int u = 0; u < kDmaPerWave; ++u) {
+        const int r = 4 * (wave_u * kDmaPerWave + u) + drow;
+        kdoff[u] = r * krs32 + ((dslot ^ (r & 15)) * 8);
+        vdoff[u] = r * vrs32 + ((dslot ^ (4 * (r & 3))) * 8);
+    }
+    // Full tile with a usable block id: asynchronous copies, waited for at the next
+    // barrier.  Issued from one asm block: M0 carries each copy's LDS address (1 KB
+    // chunk), and the compiler, which does not see these copies, adds no waits of
+    // its own for them before the LDS reads of the other buffer.  The explicit
+    // vmcnt(0) and the barrier (a workgroup fence) order them against every later
+    // read of the buffer they fill.
+    static_assert(kDmaPerWave == 4, "one asm block moves 4 K and 4 V chunks per wave");
+    auto issue_tile = [&](int t, int stage, int32_t blk) {
+        bool ok;
+        const int64_t r0 = row0_of(t, blk, ok);
+        const uint16_t* kp = kbase + r0 * krs;
+        const uint16_t* vp = vbase + r0 * vrs;
+        const uint32_t kl = (uint32_t)(uintptr_t)k_lds3 + stage * kKTileBytes + 1024 * (wave_u * kDmaPerWave);
+        const uint32_t vl = (uint32_t)(uintptr_t)v_lds3 + stage * kVTileBytes + 1024 * (wave_u * kDmaPerWave);
+        uint32_t saved;
+        asm volatile(
+            "s_mov_b32 %[sv], m0\n\t"
+            "s_mov_b32 m0, %[k0l]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[k0], off\n\t"
+            "s_mov_b32 m0, %[k1l]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[k1], off\n\t"
+            "s_mov_b32 m0, %[k2l]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[k2], off\n\t"
+            "s_mov_b32 m0, %[k3l]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[k3], off\n\t"
+            "s_mov_b32 m0, %[v0l]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v0], off\n\t"
+            "s_mov_b32 m0, %[v1l]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v1], off\n\t"
+            "s_mov_b32 m0, %[v2l]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v2], off\n\t"
+            "s_mov_b32 m0, %[v3l]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v3], off\n\t"
+            "s_mov_b32 m0, %[sv]"
+            : [sv] "=&s"(saved)
+            : [k0] "v"(kp + kdoff[0]), [k1] "v"(kp + kdoff[1]), [k2] "v"(kp + kdoff[2]), [k3] "v"(kp + kdoff[3]),
+              [v0] "v"(vp + vdoff[0]), [v1] "v"(vp + vdoff[1]), [v2] "v"(vp + vdoff[2]), [v3] "v"(vp + vdoff[3]),
+              [k0l] "s"(kl), [k1l] "s"(kl + 1024), [k2l] "s"(kl + 2048), [k3l] "s"(kl + 3072),
+              [v0l] "s"(vl), [v1l] "s"(vl + 1024), [v2l] "s"(vl + 2048), [v3l] "s"(vl + 3072));
+    };
+    // Partial or unusable tile: through registers, rows past the end clamped for K and
+    // zeroed for V (their weights are 0; zeros keep NaN-carrying slots out of P V).
+    auto fill_tile_sync = [&](int t, int stage, int32_t blk) {
+        bool ok;
+        const int64_t r0 = row0_of(t, blk, ok);
+        const int last = Lk - 1 - t * kKT;
+        const uint16_t* kp = kbase + r0 * krs;
+        const uint16_t* vp = vbase + r0 * vrs;
+#pragma unroll
+        for (int u = 0; u < kDmaPerWave; ++u) {
+            const int r = 4 * (wave_u * kDmaPerWave + u) + drow;
+            const int row = ok ? min(r, last) : 0;
+            const u32x4 kx = ldg128(kp + (row * krs32 + (dslot ^ (r & 15)) * 8));
+            u32x4 vx = ldg128(vp + (row * vrs32 + (dslot ^ (4 * (r & 3))) * 8));
+            if (!ok || r > last) vx = u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(k_lds + stage * kKTileBytes + r * 256 + dslot * 16) = kx;
+            *reinterpret_cast<u32x4*>(v_lds + stage * kVTileBytes + r * 256 + dslot * 16) = vx;
+        }
+    };
+    auto tile_full = [&](int t, int32_t blk) {
+        bool ok;
+        (void)row0_of(t, blk, ok);
+        return ok && Lk - 1 - t * kKT >= kKT - 1;
+    };
 
     const int h32 = lane >> 5;  // which half of the k-slots this lane feeds
 
@@ -269,17 +370,42 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
     //   than 2^8, so the O rescale is skipped on most tiles.  Exact for any input:
     //   O and l always share the reference.
     {
-        load_tile(0);
-        store_tile(0, k_lds, v_lds);
-        if (1 < n_tiles) load_tile(1);
-        __syncthreads();
+        bool ok_cur = false;   // fast pass: whether tile t's block id is usable, found when its copies were issued
+        int32_t blk_next = 0;  // fast pass: block id of tile t+1
+        if (kDma) {
+            const int32_t blk0 = blk_of(0, load_blk(0));
+            blk_next = load_blk(min(1, n_tiles - 1));
+            (void)row0_of(0, blk0, ok_cur);
+            if (tile_full(0, blk0)) issue_tile(0, 0, blk0); else fill_tile_sync(0, 0, blk0);
+        } else {
+            load_tile(0);
+            store_tile(0, k_lds, v_lds);
+            if (1 < n_tiles) load_tile(1);
+            __syncthreads();
+        }
         for (int t = 0; t < n_tiles; ++t) {
             unsigned char* kb = k_lds + (t & 1) * kKTileBytes;
             unsigned char* vb = v_lds + (t & 1) * kVTileBytes;
+            if (kDma) {
+                // this wave's copies of tile t have landed; after the barrier every
+                // wave's have, and every wave is done with tile t-1, whose buffer the
+                // copies of tile t+1 then fill while tile t is computed
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+                __syncthreads();
+            }
+            bool ok_next = false;
+            if (kDma && t + 1 < n_tiles) {
+                const int32_t blk = blk_of(t + 1, blk_next);
+                (void)row0_of(t + 1, blk, ok_next);
+                if (tile_full(t + 1, blk)) issue_tile(t + 1, (t + 1) & 1, blk);
+                else fill_tile_sync(t + 1, (t + 1) & 1, blk);
+                // issued after the copies: the wait for them at the next barrier covers it
+                blk_next = load_blk(min(t + 2, n_tiles - 1));
+            }
             if (t < wave_tiles) {   // this wave still has visible keys in tile t
                 const int j0 = t * kKT;
-                bool ok;
-                (void)tile_row0(t, ok);
+                bool ok = ok_cur;
+                if (!kDma) (void)tile_row0(t, ok);
                 // ---- S^T = K Q^T for the tile's 32-key blocks
                 // The key blocks are independent accumulation chains; interleaving them
                 // keeps consecutive MFMAs independent so each issues without waiting for the
@@ -293,8 +419,9 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
                 for (int st = 0; st < 8; ++st)
 #pragma unroll
                     for (int kh = 0; kh < kKH; ++kh) {
-                        const unsigned char* kr = kb + (32 * kh + (lane & 31)) * kKPitch + 16 * h32;
-                        const bf16x8 av = *reinterpret_cast<const bf16x8*>(kr + 32 * st);
+                        const unsigned char* kr = kDma ? kb + (32 * kh + (lane & 31)) * 256 + (((2 * st + h32) ^ (lane & 15)) << 4)
+                                                       : kb + (32 * kh + (lane & 31)) * kKPitch + 16 * h32 + 32 * st;
+                        const bf16x8 av = *reinterpret_cast<const bf16x8*>(kr);
                         s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[st], s[kh], 0, 0, 0);
                     }
                 // s[kh][r] = score of key j0 + 32kh + 8(r/4) + 4*h32 + r%4 for query qi
@@ -369,8 +496,11 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
 #pragma unroll
                         for (int dt = 0; dt < 4; ++dt) {
                             const int d0 = 32 * dt + 16 * (grp16 & 1) + 4 * (j16 & 3);
-                            lds_ptr_t p0 = (lds_ptr_t)(vb + (kcol + (j16 >> 2)) * kVPitch + 2 * d0);
-                            lds_ptr_t p1 = (lds_ptr_t)(vb + (kcol + 8 + (j16 >> 2)) * kVPitch + 2 * d0);
+                            // swizzled: piece (2 d0)/16 of row kcol + j16/4 (row % 4 = j16/4) sits in
+                            // slot piece ^ 4(j16/4), i.e. dims 32 dt move to 32 (dt ^ j16/4)
+                            const int vo = kDma ? 64 * (dt ^ (j16 >> 2)) + 32 * (grp16 & 1) + 8 * (j16 & 3) : 2 * d0;
+                            lds_ptr_t p0 = (lds_ptr_t)(vb + (kcol + (j16 >> 2)) * kVP + vo);
+                            lds_ptr_t p1 = (lds_ptr_t)(vb + (kcol + 8 + (j16 >> 2)) * kVP + vo);
                             const bf16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p0);
                             const bf16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p1);
                             const bf16x8 av = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -378,10 +508,13 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
                         }
                     }
             }
-            if (t + 1 < n_tiles)
-                store_tile(t + 1, k_lds + ((t + 1) & 1) * kKTileBytes, v_lds + ((t + 1) & 1) * kVTileBytes);
-            __syncthreads();
-            if (t + 2 < n_tiles) load_tile(t + 2);
+            if (!kDma) {
+                if (t + 1 < n_tiles)
+                    store_tile(t + 1, k_lds + ((t + 1) & 1) * kKTileBytes, v_lds + ((t + 1) & 1) * kVTileBytes);
+                __syncthreads();
+                if (t + 2 < n_tiles) load_tile(t + 2);
+            }
+            ok_cur = ok_next;
         }
     }
 
@@ -434,8 +567,8 @@ template <int GW, bool PAGED, int NW>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a, int32_t m_blocks, int32_t n_work,
                                                                   int32_t head_groups, int32_t chunk, uint64_t call) {
     constexpr int kKT = kTileKeys<NW>;
-    __shared__ __attribute__((aligned(16))) unsigned char k_lds[2 * kKT * kKPitch];
-    __shared__ __attribute__((aligned(16))) unsigned char v_lds[2 * kKT * kVPitch];
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds[2 * kKT * kHeadDim * 2];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds[2 * kKT * kHeadDim * 2];
 
     // Chunks of `chunk` consecutive work items are dealt round-robin over the 8
     // XCDs, which take workgroups round-robin by id: XCD x runs chunks x, x+8,
@@ -497,12 +630,13 @@ hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t stream) {
     const int64_t grid64 = ((n_chunks + 7) / 8) * 8 * chunk;
     if (grid64 > (int64_t)0x7FFFFFF0) return hipErrorInvalidValue;
     const int grid = (int)grid64;
-    // Batches under 2.5e11 FLOP (counted without the causal half, so roughly
-    // under 150 us of work) run the exact pass alone in one launch: there the
-    // second launch of the two-pass scheme (~4 us when nothing is flagged) costs
-    // about what the fast pass saves (measured: 5% slower at 4 x 512 tokens, even
-    // at 8 x 1024, 4% faster on 16 x 2048 queries over 4096 keys).
-    const bool two_pass = (double)a.total_q * a.max_seqlen_k * a.hq * 4.0 * kHeadDim >= 2.5e11;
+    // Batches under 2e10 FLOP (counted without the causal half, so roughly under
+    // 20 us of work) run the exact pass alone in one launch: there the second
+    // launch of the two-pass scheme (~4 us when nothing is flagged) costs more than
+    // the fast pass saves (measured: two passes 10% slower at 16 x 128 tokens,
+    // even at 4 x 512, 7-9% faster from 8 x 1024 and on 16 x 2048 queries over
+    // 4096 keys).
+    const bool two_pass = (double)a.total_q * a.max_seqlen_k * a.hq * 4.0 * kHeadDim >= 2e10;
     // Exact pass after the fast one: one workgroup per CU slot (two 4-wave or one
     // 8-wave per CU), walking the work items.
     const int grid_exact = two_pass ? (int)std::min<int64_t>(n_work64, nw == 8 ? 256 : 512) : grid;
