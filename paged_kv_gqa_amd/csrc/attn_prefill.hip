@@ -70,9 +70,10 @@ constexpr int kRowsPerWave = 32;
 constexpr int kKPitch = kHeadDim * 2 + 16;  // bytes per K row in LDS (row-major)
 constexpr int kVPitch = kHeadDim * 2 + 64;  // bytes per V row in LDS (row-major, read transposed)
 constexpr float kLazyLog2 = 8.0f;           // the lazy reference max moves when a row grows by > 2^8
-// Keys per tile: 128 for the 8-wave workgroup (one per CU, LDS for two 74 KB
-// tile pairs), 64 for 4 waves (two workgroups per CU).  A tile never straddles
-// a 256-token block.
+// Keys per tile: 128 for the 8-wave workgroup (one per CU; LDS for two K+V tile
+// pairs: 64 KB each unpadded in the fast pass, 74 KB padded in the exact pass),
+// 64 for 4 waves (two workgroups per CU).  A tile never straddles a 256-token
+// block.
 template <int NW>
 constexpr int kTileKeys = NW == 8 ? 128 : 64;
 // Left by the fast pass in the first output element of a wave whose rows need
@@ -85,9 +86,6 @@ constexpr uint16_t kFixupMarker = 0x7F81;
 // item; raised with a device-scope atomic, never lowered.  The exact pass of a
 // call scans for markers only when this is at least its own number.
 __device__ unsigned long long g_prefill_flagged_call = 0;
-
-namespace {
-}  // namespace
 
 // One work item: query block mb of (sequence b, kv head g, head group hg), with
 // NW waves (4 or 8; two waves per SIMD either way: two workgroups of 4 per CU,
@@ -175,12 +173,13 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
     }
     const int qpos = off + qi;                          // absolute position of this lane's query
 
-    // ---- tile loader.  Thread tid moves 16-byte piece tid%16 of rows tid/16 + kLoadRows*i
-    // (i < kLoadIters) of the K and V tiles.  Row offsets are loop-invariant; every
-    // load is issued on every path (rows past the last key are clamped onto it), so
-    // the compiler's wait counts stay exact.
-    // Row strides are at most 2^24 elements (checked by the caller), so offsets
-    // inside one tile fit in 32 bits: a per-tile base plus a 32-bit lane offset.
+    // ---- tile loaders.  Row strides are at most 2^24 elements (checked by the
+    // caller), so offsets inside one tile fit in 32 bits: a per-tile base plus a
+    // 32-bit lane offset.
+    // Exact pass (through registers): thread tid moves 16-byte piece tid%16 of rows
+    // tid/16 + kLoadRows*i (i < kLoadIters) of the K and V tiles.  Row offsets are
+    // loop-invariant; every load is issued on every path (rows past the last key are
+    // clamped onto it), so the compiler's wait counts stay exact.
     const int64_t krs = a.k_row_stride, vrs = a.v_row_stride;
     const int32_t krs32 = (int32_t)krs, vrs32 = (int32_t)vrs;
     const uint16_t* kbase = (const uint16_t*)a.k + (int64_t)g * kHeadDim;
@@ -355,9 +354,10 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
     const float lazy_raw = kLazyLog2 / a.scale_log2;
 
     // One pass over the key tiles.  Double-buffered LDS tiles: one barrier per tile.
-    // Tile t is computed from buffer t&1 while tile t+1 (loaded into registers one
-    // iteration earlier) is stored into the other buffer; tile t+2 is loaded after
-    // the barrier.
+    // Exact pass: tile t is computed from buffer t&1 while tile t+1 (loaded into
+    // registers one iteration earlier) is stored into the other buffer; tile t+2 is
+    // loaded after the barrier.  Fast pass: right after the barrier, tile t+1 is
+    // copied straight into the other buffer while tile t is computed.
     //   Fast pass (kExact false): Q pre-scaled, the weights are exp2(score) against
     //   a fixed reference of 0 -- no row max, no rescale, one VALU op less per score.
     //   Softmax does not depend on the reference and floating point is
@@ -419,8 +419,11 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
                 for (int st = 0; st < 8; ++st)
 #pragma unroll
                     for (int kh = 0; kh < kKH; ++kh) {
-                        const unsigned char* kr = kDma ? kb + (32 * kh + (lane & 31)) * 256 + (((2 * st + h32) ^ (lane & 15)) << 4)
-                                                       : kb + (32 * kh + (lane & 31)) * kKPitch + 16 * h32 + 32 * st;
+                        // piece 2st + h32 of row 32kh + lane%32; swizzled, it sits in slot
+                        // piece ^ (row % 16) = piece ^ (lane % 16)
+                        const unsigned char* kr =
+                            kDma ? kb + (32 * kh + (lane & 31)) * 256 + (((2 * st + h32) ^ (lane & 15)) << 4)
+                                 : kb + (32 * kh + (lane & 31)) * kKPitch + 16 * h32 + 32 * st;
                         const bf16x8 av = *reinterpret_cast<const bf16x8*>(kr);
                         s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[st], s[kh], 0, 0, 0);
                     }
