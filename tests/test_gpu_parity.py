@@ -301,6 +301,47 @@ def test_prefill_scores_outside_fast_range(dev, kind, lens_q, lens_k, hq, hkv, p
     check_attn(got, ref, f"prefill {kind} scores")
 
 
+def test_prefill_flagged_and_clean_calls_on_two_streams(dev):
+    """Two-pass prefill calls in flight together on two streams, one with rows that
+    leave the fast pass's range and one without: each call's exact pass must find
+    its own flags (the device keeps the highest flagged call number), whatever
+    order the calls run in; the clean call may scan but stays exact."""
+    _say("prefill: flagged and clean two-pass calls interleaved on two streams")
+    hq, hkv = 32, 8
+    lens_a, lens_b = [4096, 4096], [2048] * 4
+    rng = wl.rng_for(92, 77, 0)
+    qa, ka, va = _extreme_scores(hq, hkv, "large")(rng, sum(lens_a), sum(lens_a))
+    qb = wl.normal_bf16(rng, (sum(lens_b), hq, D))
+    kb = wl.normal_bf16(rng, (sum(lens_b), hkv, D))
+    vb = wl.normal_bf16(rng, (sum(lens_b), hkv, D))
+    cua, cub = wl.cu_seqlens(lens_a), wl.cu_seqlens(lens_b)
+    da = [to_dev(x, dev) for x in (qa, ka, va, cua)]
+    db = [to_dev(x, dev) for x in (qb, kb, vb, cub)]
+    oa = torch.empty_like(da[0])
+    ob = torch.empty_like(db[0])
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for first in ("a", "b", "a"):
+        oa.fill_(0)
+        ob.fill_(0)
+        torch.cuda.synchronize()
+        order = [("a", s1), ("b", s2)] if first == "a" else [("b", s2), ("a", s1)]
+        for which, st in order:
+            with torch.cuda.stream(st):
+                if which == "a":
+                    pkv.attn_prefill_varlen(da[0], da[1], da[2], da[3], da[3], 4096, 4096, out=oa)
+                else:
+                    pkv.attn_prefill_varlen(db[0], db[1], db[2], db[3], db[3], 2048, 2048, out=ob)
+        torch.cuda.synchronize()
+        for q, k, v, cu, o, lens in ((qa, ka, va, cua, oa, lens_a), (qb, kb, vb, cub, ob, lens_b)):
+            t = np.arange(0, sum(lens), 41)
+            rows = np.concatenate([np.stack([t, np.zeros_like(t)], 1), np.stack([t, np.full_like(t, hq - 1)], 1)])
+            ref = oracle.attn_prefill(q, k, v, cu, cu, hq, hkv, rows=rows)
+            got = f64(o)[rows[:, 0], rows[:, 1]]
+            assert np.isfinite(got).all()
+            check_attn(got, ref, f"two streams, {first} first")
+
+
 def test_prefill_paged_prefix(dev):
     lk, lq = [300, 513, 64, 1000], [40, 257, 64, 1]
     _say(f"prefill case 2 (paged), Lk {lk}, Lq {lq}")
