@@ -31,8 +31,9 @@
 //   * Double-buffered LDS, one barrier per tile.  Tiles (128 keys with 8
 //     waves, 64 with 4) never straddle a 256-token block, so the paged loader
 //     does one block-table lookup per tile.  The fast pass copies each tile
-//     straight from global memory into LDS (global_load_lds_dwordx4, issued
-//     right after the barrier for the next tile while this one is computed):
+//     straight from global memory into LDS (global_load_lds_dwordx4, for the
+//     next tile while this one is computed: K right after the barrier, V after
+//     the QK^T phase):
 //     no staging registers and no LDS store instructions; rows are unpadded
 //     with 16-byte slots XOR-swizzled per row so the operand reads stay
 //     conflict-free.  The exact pass stages tiles through registers into padded
@@ -287,36 +288,31 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
         vdoff[u] = r * vrs32 + ((dslot ^ (4 * (r & 3))) * 8);
     }
     // Full tile with a usable block id: asynchronous copies, waited for at the next
-    // barrier.  Issued from one asm block: M0 carries each copy's LDS address (1 KB
-    // chunk), and the compiler, which does not see these copies, adds no waits of
-    // its own for them before the LDS reads of the other buffer.  The explicit
-    // vmcnt(0) and the barrier (a workgroup fence) order them against every later
-    // read of the buffer they fill.
-    static_assert(kDmaPerWave == 4, "one asm block moves 4 K and 4 V chunks per wave");
-    auto issue_tile = [&](int t, int stage, int32_t blk) {
+    // barrier -- the K half right after the barrier, the V half after the QK^T phase
+    // (spreading the LDS writes over the tile: measured +2%).  Each half is one asm
+    // block: M0 carries each copy's LDS address (1 KB chunk), and the compiler, which
+    // does not see these copies, adds no waits of its own for them before the LDS
+    // reads of the other buffer.  The explicit vmcnt(0) and the barrier (a
+    // workgroup fence) order them against every later read of the buffer they fill.
+    static_assert(kDmaPerWave == 4, "one asm block moves a wave's 4 chunks of K or of V");
+    auto issue_half = [&](int t, int stage, int32_t blk, bool vhalf) {
         bool ok;
         const int64_t r0 = row0_of(t, blk, ok);
-        const uint16_t* kp = kbase + r0 * krs;
-        const uint16_t* vp = vbase + r0 * vrs;
-        const uint32_t kl = (uint32_t)(uintptr_t)k_lds3 + stage * kKTileBytes + 1024 * (wave_u * kDmaPerWave);
-        const uint32_t vl = (uint32_t)(uintptr_t)v_lds3 + stage * kVTileBytes + 1024 * (wave_u * kDmaPerWave);
+        const uint16_t* p = (vhalf ? vbase : kbase) + r0 * (vhalf ? vrs : krs);
+        const int32_t* off = vhalf ? vdoff : kdoff;
+        const uint32_t l = (uint32_t)(uintptr_t)(vhalf ? v_lds3 : k_lds3) +
+                           stage * (vhalf ? kVTileBytes : kKTileBytes) + 1024 * (wave_u * kDmaPerWave);
         uint32_t saved;
         asm volatile(
             "s_mov_b32 %[sv], m0\n\t"
-            "s_mov_b32 m0, %[k0l]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[k0], off\n\t"
-            "s_mov_b32 m0, %[k1l]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[k1], off\n\t"
-            "s_mov_b32 m0, %[k2l]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[k2], off\n\t"
-            "s_mov_b32 m0, %[k3l]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[k3], off\n\t"
-            "s_mov_b32 m0, %[v0l]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v0], off\n\t"
-            "s_mov_b32 m0, %[v1l]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v1], off\n\t"
-            "s_mov_b32 m0, %[v2l]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v2], off\n\t"
-            "s_mov_b32 m0, %[v3l]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v3], off\n\t"
+            "s_mov_b32 m0, %[l0]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[a0], off\n\t"
+            "s_mov_b32 m0, %[l1]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[a1], off\n\t"
+            "s_mov_b32 m0, %[l2]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[a2], off\n\t"
+            "s_mov_b32 m0, %[l3]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[a3], off\n\t"
             "s_mov_b32 m0, %[sv]"
             : [sv] "=&s"(saved)
-            : [k0] "v"(kp + kdoff[0]), [k1] "v"(kp + kdoff[1]), [k2] "v"(kp + kdoff[2]), [k3] "v"(kp + kdoff[3]),
-              [v0] "v"(vp + vdoff[0]), [v1] "v"(vp + vdoff[1]), [v2] "v"(vp + vdoff[2]), [v3] "v"(vp + vdoff[3]),
-              [k0l] "s"(kl), [k1l] "s"(kl + 1024), [k2l] "s"(kl + 2048), [k3l] "s"(kl + 3072),
-              [v0l] "s"(vl), [v1l] "s"(vl + 1024), [v2l] "s"(vl + 2048), [v3l] "s"(vl + 3072));
+            : [a0] "v"(p + off[0]), [a1] "v"(p + off[1]), [a2] "v"(p + off[2]), [a3] "v"(p + off[3]),
+              [l0] "s"(l), [l1] "s"(l + 1024), [l2] "s"(l + 2048), [l3] "s"(l + 3072));
     };
     // Partial or unusable tile: through registers, rows past the end clamped for K and
     // zeroed for V (their weights are 0; zeros keep NaN-carrying slots out of P V).
@@ -376,7 +372,8 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
             const int32_t blk0 = blk_of(0, load_blk(0));
             blk_next = load_blk(min(1, n_tiles - 1));
             (void)row0_of(0, blk0, ok_cur);
-            if (tile_full(0, blk0)) issue_tile(0, 0, blk0); else fill_tile_sync(0, 0, blk0);
+            if (tile_full(0, blk0)) { issue_half(0, 0, blk0, false); issue_half(0, 0, blk0, true); }
+            else fill_tile_sync(0, 0, blk0);
         } else {
             load_tile(0);
             store_tile(0, k_lds, v_lds);
@@ -394,23 +391,27 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
                 __syncthreads();
             }
             bool ok_next = false;
+            bool v_later = false;   // V copies of tile t+1 issued after the QK^T phase
+            int32_t blk1 = 0;
             if (kDma && t + 1 < n_tiles) {
                 const int32_t blk = blk_of(t + 1, blk_next);
+                blk1 = blk;
                 (void)row0_of(t + 1, blk, ok_next);
-                if (tile_full(t + 1, blk)) issue_tile(t + 1, (t + 1) & 1, blk);
+                if (tile_full(t + 1, blk)) { issue_half(t + 1, (t + 1) & 1, blk, false); v_later = true; }
                 else fill_tile_sync(t + 1, (t + 1) & 1, blk);
                 // issued after the copies: the wait for them at the next barrier covers it
                 blk_next = load_blk(min(t + 2, n_tiles - 1));
             }
-            if (t < wave_tiles) {   // this wave still has visible keys in tile t
-                const int j0 = t * kKT;
-                bool ok = ok_cur;
-                if (!kDma) (void)tile_row0(t, ok);
+            const bool live_t = t < wave_tiles;   // this wave still has visible keys in tile t
+            const int j0 = t * kKT;
+            bool ok = ok_cur;
+            if (!kDma) (void)tile_row0(t, ok);
+            f32x16 s[kKH];
+            if (live_t) {
                 // ---- S^T = K Q^T for the tile's 32-key blocks
                 // The key blocks are independent accumulation chains; interleaving them
                 // keeps consecutive MFMAs independent so each issues without waiting for the
                 // previous result.
-                f32x16 s[kKH];
 #pragma unroll
                 for (int kh = 0; kh < kKH; ++kh)
 #pragma unroll
@@ -438,6 +439,9 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
                     }
                     __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
                 }
+            }
+            if (v_later) issue_half(t + 1, (t + 1) & 1, blk1, true);
+            if (live_t) {
                 // s[kh][r] = score of key j0 + 32kh + 8(r/4) + 4*h32 + r%4 for query qi
                 // (base-2 units in the fast pass, raw in the exact pass).
                 const bool need_mask = !ok || (j0 + kKT - 1 > off + wp0) || (j0 + kKT > Lk);
@@ -555,17 +559,20 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
     }
 
     // ---- normalise and store: lane holds O^T[d][qi] for d = 32dt + 8(r/4) + 4*h32 + r%4.
-    if (!wave_live || qi >= Lq) return;
+    // (the lane's row and half are recomputed here rather than kept across the loop)
+    const int lane_e = __lane_id();
+    const int qi_e = wp0 + (lane_e & 31), h32_e = lane_e >> 5;
+    if (!wave_live || qi_e >= Lq) return;
     const float l = l_part + __shfl_xor(l_part, 32, 64);
     const float inv = l > 0.f ? 1.0f / l : 0.f;
-    const int orow = cq0 + qi;
+    const int orow = cq0 + qi_e;
     if (orow >= a.total_q) return;
     uint16_t* op = (uint16_t*)a.o + ((int64_t)orow * a.hq + head) * kHeadDim;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-            const int d = 32 * dt + 8 * r4 + 4 * h32;
+            const int d = 32 * dt + 8 * r4 + 4 * h32_e;
             u32x2 w;
             w[0] = pack_bf16x2(oacc[dt][4 * r4] * inv, oacc[dt][4 * r4 + 1] * inv);
             w[1] = pack_bf16x2(oacc[dt][4 * r4 + 2] * inv, oacc[dt][4 * r4 + 3] * inv);
