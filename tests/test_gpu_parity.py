@@ -615,6 +615,39 @@ def test_decode_row_equals_prefill_row(dev):
     assert err.max() <= 2e-2, err.max()
 
 
+@pytest.mark.parametrize("bad_id", [-1, 10 ** 6])
+def test_prefill_unusable_block_id_drops_its_keys(dev, bad_id):
+    """Case 2 prefill (large enough for the fast pass, 4-wave workgroups) whose block
+    tables hold an unusable id (-1, or past the pool) for block 1 of every sequence:
+    those 256 keys are never read and drop out of the softmax.  Every query sits past
+    block 1, so its result equals a decode over the same table with that entry
+    removed and the context shortened by 256 (attention depends only on the set of
+    visible keys)."""
+    _say(f"prefill case 2 with block id {bad_id} in block 1 of every sequence")
+    rng = wl.rng_for(99, 1 if bad_id < 0 else 2, 0)
+    hq, hkv, B, lq, lk = 32, 8, 8, 1000, 3000
+    nbs = -(-lk // 256)
+    nb = B * nbs
+    kc = wl.normal_bf16(rng, (nb, 256, hkv, D))
+    vc = wl.normal_bf16(rng, (nb, 256, hkv, D))
+    q = wl.normal_bf16(rng, (B * lq, hq, D))
+    bt = rng.permutation(nb).astype(np.int32).reshape(B, nbs)
+    bt_bad = bt.copy()
+    bt_bad[:, 1] = bad_id
+    cuq, cuk = wl.cu_seqlens([lq] * B), wl.cu_seqlens([lk] * B)
+    o = pkv.attn_prefill_varlen(to_dev(q, dev), to_dev(kc, dev), to_dev(vc, dev), to_dev(cuq, dev), to_dev(cuk, dev),
+                                lq, lk, block_table=to_dev(bt_bad, dev))
+    torch.cuda.synchronize()
+    t = np.arange(0, B * lq, 37)
+    b, i = t // lq, t % lq
+    bt_drop = np.concatenate([bt[:, :1], bt[:, 2:], np.zeros((B, 1), np.int32)], 1)[b]   # block 1 removed
+    ctx = (lk - lq + i + 1 - 256).astype(np.int32)
+    got = f64(o)[t]                                                                      # [rows, hq, d]
+    ref = oracle.attn_decode(q[t], kc.reshape(-1, hkv, D), vc.reshape(-1, hkv, D), ctx, bt_drop, hq, hkv)
+    assert np.isfinite(got).all()
+    check_attn(got, ref, f"prefill with block id {bad_id}")
+
+
 def test_decode_unusable_block_ids_drop_their_keys(dev):
     """A block id of -1 or past the pool inside the context: its keys are never read and
     drop out of the softmax (the documented behaviour for invalid metadata).  With the
