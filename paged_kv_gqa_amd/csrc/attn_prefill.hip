@@ -280,17 +280,20 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
     constexpr int kDmaPerWave = kKT / 4 / NW;
     const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int drow = lane >> 4, dslot = lane & 15;
-    int32_t kdoff[kDmaPerWave], vdoff[kDmaPerWave];
+    // byte offsets from the tile's first row (< 127 * 2^25 + 256: fit 32 bits unsigned)
+    uint32_t kdoff[kDmaPerWave], vdoff[kDmaPerWave];
 #pragma unroll
     for (int u = 0; u < kDmaPerWave; ++u) {
         const int r = 4 * (wave_u * kDmaPerWave + u) + drow;
-        kdoff[u] = r * krs32 + ((dslot ^ (r & 15)) * 8);
-        vdoff[u] = r * vrs32 + ((dslot ^ (4 * (r & 3))) * 8);
+        kdoff[u] = 2u * (uint32_t)(r * krs32 + ((dslot ^ (r & 15)) * 8));
+        vdoff[u] = 2u * (uint32_t)(r * vrs32 + ((dslot ^ (4 * (r & 3))) * 8));
     }
     // Full tile with a usable block id: asynchronous copies, waited for at the next
     // barrier -- the K half right after the barrier, the V half after the QK^T phase
     // (spreading the LDS writes over the tile: measured +2%).  Each half is one asm
-    // block: M0 carries each copy's LDS address (1 KB chunk), and the compiler, which
+    // block: the scalar-base form (tile base in SGPRs + the lane's 32-bit byte offset:
+    // no address arithmetic per tile), M0 carries each copy's LDS address (1 KB
+    // chunk), and the compiler, which
     // does not see these copies, adds no waits of its own for them before the LDS
     // reads of the other buffer.  The explicit vmcnt(0) and the barrier (a
     // workgroup fence) order them against every later read of the buffer they fill.
@@ -298,20 +301,20 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
     auto issue_half = [&](int t, int stage, int32_t blk, bool vhalf) {
         bool ok;
         const int64_t r0 = row0_of(t, blk, ok);
-        const uint16_t* p = (vhalf ? vbase : kbase) + r0 * (vhalf ? vrs : krs);
-        const int32_t* off = vhalf ? vdoff : kdoff;
+        const uint16_t* p = (vhalf ? vbase : kbase) + r0 * (vhalf ? vrs : krs);   // uniform: a scalar base
+        const uint32_t* off = vhalf ? vdoff : kdoff;
         const uint32_t l = (uint32_t)(uintptr_t)(vhalf ? v_lds3 : k_lds3) +
                            stage * (vhalf ? kVTileBytes : kKTileBytes) + 1024 * (wave_u * kDmaPerWave);
         uint32_t saved;
         asm volatile(
             "s_mov_b32 %[sv], m0\n\t"
-            "s_mov_b32 m0, %[l0]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[a0], off\n\t"
-            "s_mov_b32 m0, %[l1]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[a1], off\n\t"
-            "s_mov_b32 m0, %[l2]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[a2], off\n\t"
-            "s_mov_b32 m0, %[l3]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[a3], off\n\t"
+            "s_mov_b32 m0, %[l0]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[a0], %[base]\n\t"
+            "s_mov_b32 m0, %[l1]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[a1], %[base]\n\t"
+            "s_mov_b32 m0, %[l2]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[a2], %[base]\n\t"
+            "s_mov_b32 m0, %[l3]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[a3], %[base]\n\t"
             "s_mov_b32 m0, %[sv]"
             : [sv] "=&s"(saved)
-            : [a0] "v"(p + off[0]), [a1] "v"(p + off[1]), [a2] "v"(p + off[2]), [a3] "v"(p + off[3]),
+            : [a0] "v"(off[0]), [a1] "v"(off[1]), [a2] "v"(off[2]), [a3] "v"(off[3]), [base] "s"(p),
               [l0] "s"(l), [l1] "s"(l + 1024), [l2] "s"(l + 2048), [l3] "s"(l + 3072));
     };
     // Partial or unusable tile: through registers, rows past the end clamped for K and
