@@ -58,6 +58,22 @@ def recorded_traffic(profile_name: str, source: str):
     return int(m_val.group(1))
 
 
+def input_checksum(torch, named):
+    """sha256 (first 16 hex digits) over each input's name, shape, dtype and the sum of its
+    32-bit words (device reduction in 64 MiB pieces, int64 accumulate).  Recorded with the
+    seed so a run's synthetic inputs can be told apart from another's."""
+    import hashlib
+    h = hashlib.sha256()
+    for name, t in named:
+        flat = t.reshape(-1).view(torch.int32) if t.element_size() * t.numel() % 4 == 0 else t.reshape(-1)
+        total = 0
+        step = 1 << 24
+        for i in range(0, flat.numel(), step):
+            total += int(torch.sum(flat[i:i + step], dtype=torch.int64).item())
+        h.update(f"{name}:{tuple(t.shape)}:{t.dtype}:{total};".encode())
+    return h.hexdigest()[:16]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +159,13 @@ def main():
                      dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
+    checksum = input_checksum(torch, [
+        ("prefill.qkv", qkv_p), ("prefill.k_cache", kc_p), ("prefill.v_cache", vc_p), ("prefill.positions", pos_p),
+        ("prefill.slot_mapping", slot_p), ("prefill.cu_seqlens_q", cuq_p), ("prefill.cu_seqlens_k", cuk_p),
+        ("prefill.block_tables", bt_p), ("decode.qkv", qkv_d), ("decode.k_cache", kc_d), ("decode.v_cache", vc_d),
+        ("decode.positions", pos_d), ("decode.slot_mapping", slot_d), ("decode.context_lens", cl_d),
+        ("decode.block_tables", bt_d)])
+    log(f"inputs: seed {args.seed}, checksum {checksum}")
     qv_p = qkv_p[:, q0:k0].view(Tq, s8.num_q_heads, D)
     kv_p = qkv_p[:, k0:v0].view(Tq, s8.num_kv_heads, D)
     vv_p = qkv_p[:, v0:].view(Tq, s8.num_kv_heads, D)
@@ -265,6 +288,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
+        "inputs": {"seed": args.seed, "checksum": checksum},
         "config": {
             "workload": "qwen3-8b attention core: paged decode (256 seqs, ctx log-U[1024,32768], 64 share an "
                         "8-block prefix) + prefix-hit causal prefill (16 x 4096 tokens, 2048 cached)",
