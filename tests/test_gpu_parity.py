@@ -225,6 +225,54 @@ def test_prefill_varlen_ragged(dev, hq, hkv):
     check_attn(f64(o), ref, "prefill ragged")
 
 
+@pytest.mark.parametrize("lens_q,lens_k,paged", [
+    ([0, 1500, 0, 1200, 7, 0], [0, 1500, 0, 1200, 7, 0], False),      # case 1: empty sequences between others
+    ([0, 700, 0, 900, 0], [512, 1400, 300, 900, 0], True),            # case 2: cached keys but no new queries
+])
+def test_prefill_zero_length_sequences(dev, lens_q, lens_k, paged):
+    """Sequences with no queries inside a batch produce no rows and leave the other
+    sequences' rows as the oracle computes them.  32/8 heads and these sizes take the
+    two-launch path (fast pass, then the exact pass), so both kernels meet the empty entries."""
+    _say(f"prefill with zero-length sequences: q {lens_q}, k {lens_k}, paged={paged}")
+    o, ref, _ = _prefill_case(dev, lens_q, lens_k, 32, 8, seed=41 + paged, paged=paged)
+    assert o.shape[0] == sum(lens_q)
+    check_attn(f64(o), ref, "prefill with empty sequences")
+
+
+def test_empty_calls_through_the_binding(dev):
+    """Zero tokens / zero sequences: every entry point of the attention core returns
+    without error, returns empty outputs and leaves the caches untouched."""
+    _say("empty calls: qk_norm_rope, qk_norm_rope_store, store_kvcache, prefill, decode")
+    hq, hkv = 16, 8
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    q, k, v = torch.empty((0, hq, D), **bf), torch.empty((0, hkv, D), **bf), torch.empty((0, hkv, D), **bf)
+    pos = torch.empty((0,), dtype=torch.int64, device=dev)
+    slots = torch.empty((0,), dtype=torch.int32, device=dev)
+    g = torch.ones((D,), **bf)
+    table = pkv.rope_cache_build(4096, D, 1e6, device=dev)
+    kc = torch.randn((2, 256, hkv, D), device=dev).to(torch.bfloat16)
+    vc = torch.randn((2, 256, hkv, D), device=dev).to(torch.bfloat16)
+    kc0, vc0 = kc.clone(), vc.clone()
+    qo, ko = pkv.qk_norm_rope(q, k, pos, g, g, table, 1e-6)
+    assert qo.shape == (0, hq, D) and ko.shape == (0, hkv, D)
+    qo = pkv.qk_norm_rope_store(q, k, v, pos, g, g, table, kc, vc, slots, 1e-6)
+    assert qo.shape == (0, hq, D)
+    pkv.store_kvcache(k, v, kc, vc, slots)
+    cu = torch.zeros((1,), dtype=torch.int32, device=dev)
+    o = pkv.attn_prefill_varlen(q, k, v, cu, cu, 0, 0)
+    assert o.shape == (0, hq, D)
+    cu3 = torch.zeros((4,), dtype=torch.int32, device=dev)            # three sequences, all empty
+    o = pkv.attn_prefill_varlen(q, kc, vc, cu3, cu3, 0, 0,
+                                block_table=torch.full((3, 2), -1, dtype=torch.int32, device=dev))
+    assert o.shape == (0, hq, D)
+    od = pkv.attn_decode_paged(q, kc, vc, torch.empty((0,), dtype=torch.int32, device=dev),
+                               torch.empty((0, 2), dtype=torch.int32, device=dev))
+    assert od.shape == (0, hq, D)
+    torch.cuda.synchronize()
+    assert torch.equal(kc.view(torch.int16), kc0.view(torch.int16))
+    assert torch.equal(vc.view(torch.int16), vc0.view(torch.int16))
+
+
 @pytest.mark.parametrize("lens,hq,hkv", [([2100, 2500, 2048, 2300], 16, 8), ([2200, 3100], 32, 8), ([2048] * 3, 8, 4),
                                          ([2100, 2300], 64, 8), ([2048], 8, 8)])
 def test_prefill_long_sequences_wide_workgroups(dev, lens, hq, hkv):
