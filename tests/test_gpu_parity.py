@@ -239,6 +239,67 @@ def test_prefill_zero_length_sequences(dev, lens_q, lens_k, paged):
     check_attn(f64(o), ref, "prefill with empty sequences")
 
 
+def test_cache_offsets_past_2_31_elements(dev):
+    """A 9000-block pool (4.7 GB per cache at 8 kv heads): blocks past 8192 start beyond
+    2^31 elements, so every cache address must be formed in 64 bits.  The same contents
+    placed at the end of the large pool give byte-identical prefill output, and both
+    scatters write the same bytes there as the oracle / a compact pool."""
+    hq, hkv, nb_big = 32, 8, 9000
+    _say(f"cache offsets past 2^31 elements: {nb_big}-block pool, prefill case 2 and both scatters")
+    lens_q, lens_k = [600, 300], [1500, 900]
+    o_small, ref, (q, kc, vc, cuq, cuk, bt) = _prefill_case(dev, lens_q, lens_k, hq, hkv, seed=77, paged=True)
+    nb_small = kc.shape[0] // 256
+    base = nb_big - nb_small - 24                      # > 8192: element offsets past 2^31
+    big_k = torch.empty((nb_big, 256, hkv, D), dtype=torch.bfloat16, device=dev)
+    big_v = torch.empty_like(big_k)
+    big_k[base:base + nb_small] = to_dev(kc.reshape(nb_small, 256, hkv, D), dev)
+    big_v[base:base + nb_small] = to_dev(vc.reshape(nb_small, 256, hkv, D), dev)
+    bt_big = np.where(bt >= 0, bt + base, -1).astype(np.int32)
+    o_big = pkv.attn_prefill_varlen(to_dev(q, dev), big_k, big_v, to_dev(cuq, dev), to_dev(cuk, dev),
+                                    max(lens_q), max(lens_k), block_table=to_dev(bt_big, dev))
+    torch.cuda.synchronize()
+    assert torch.equal(o_big.view(torch.int16), o_small.view(torch.int16)), "output depends on where the blocks sit"
+    check_attn(f64(o_big), ref, "prefill, blocks past 2^31 elements")
+
+    # scatter: 300 tokens into the last 10 blocks (zeroed first), against the oracle scatter
+    rng = wl.rng_for(93, 3, 0)
+    n, tail = 300, 10
+    key, val = wl.normal_bf16(rng, (n, hkv, D)), wl.normal_bf16(rng, (n, hkv, D))
+    local = rng.permutation(tail * 256)[:n].astype(np.int32)
+    local[:3] = [-1 - (nb_big - tail) * 256, 0, tail * 256 - 1]   # first maps to slot -1
+    slots = (local + (nb_big - tail) * 256).astype(np.int32)
+    big_k[nb_big - tail:].zero_()
+    big_v[nb_big - tail:].zero_()
+    pkv.store_kvcache(to_dev(key, dev), to_dev(val, dev), big_k, big_v, to_dev(slots, dev))
+    ek = np.zeros((tail * 256, hkv, D), np.uint16)
+    ev = np.zeros_like(ek)
+    oracle.store_kvcache(key, val, ek, ev, np.where(slots >= 0, local, -1).astype(np.int32))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(big_k[nb_big - tail:]).reshape(ek.shape), ek)
+    assert np.array_equal(bits(big_v[nb_big - tail:]).reshape(ev.shape), ev)
+
+    # fused QK-Norm + RoPE + scatter: the same bytes as into a compact pool of `tail` blocks
+    qkv = wl.normal_bf16(rng, (n, (hq + 2 * hkv) * D))
+    q0, k0, v0 = hq * D, (hq + hkv) * D, (hq + 2 * hkv) * D
+    qkv_d = to_dev(qkv, dev)
+    qv, kv, vv = (qkv_d[:, :q0].view(n, hq, D), qkv_d[:, q0:k0].view(n, hkv, D), qkv_d[:, k0:v0].view(n, hkv, D))
+    pos = to_dev(rng.integers(0, 40960, size=n).astype(np.int64), dev)
+    g = to_dev(wl.gamma_bf16(rng), dev)
+    table = pkv.rope_cache_build(40960, D, 1e6, device=dev)
+    big_k[nb_big - tail:].zero_()
+    big_v[nb_big - tail:].zero_()
+    qa = pkv.qk_norm_rope_store(qv, kv, vv, pos, g, g, table, big_k, big_v, to_dev(slots, dev), 1e-6)
+    ck = torch.zeros((tail, 256, hkv, D), dtype=torch.bfloat16, device=dev)
+    cv = torch.zeros_like(ck)
+    qb = pkv.qk_norm_rope_store(qv, kv, vv, pos, g, g, table, ck, cv,
+                                to_dev(np.where(slots >= 0, local, -1).astype(np.int32), dev), 1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(qa.view(torch.int16), qb.view(torch.int16))
+    assert torch.equal(big_k[nb_big - tail:].view(torch.int16), ck.view(torch.int16))
+    assert torch.equal(big_v[nb_big - tail:].view(torch.int16), cv.view(torch.int16))
+    del big_k, big_v
+
+
 def test_empty_calls_through_the_binding(dev):
     """Zero tokens / zero sequences: every entry point of the attention core returns
     without error, returns empty outputs and leaves the caches untouched."""
