@@ -269,11 +269,12 @@ def main():
     ladder = decode_graph_ladder(pkv, torch, s8, table, qkv_d, kc_d, vc_d, pos_d, slot_d, cl_d, bt_d, gq_d, gk_d,
                                  args, log)
 
-    cpu = cpu_pre = cpu_st = None
+    cpu = cpu_pre = cpu_st = cpu_one = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, wd, kc_d, vc_d, qo_d, log)
         cpu_pre = cpu_baseline_prefill(args, wp, kc_p, vc_p, qo_p, log)
         cpu_st = cpu_stages(args, wp, qkv_p, log)
+        cpu_one = cpu_one_thread(args, log)
 
     out = {
         "metric": METRIC,
@@ -314,6 +315,7 @@ def main():
         "decode_graph": ladder,
         "cpu_baseline_prefill": cpu_pre,
         "cpu_baseline_stages": cpu_st,
+        "cpu_baseline_one_thread": cpu_one,
     }
     print(json.dumps(out), flush=True)
 
@@ -560,6 +562,83 @@ def cpu_stages(args, wp, qkv_p, log):
            "cores": oracle.num_threads(), "kind": "oracle",
            "sample": f"first {n} tokens of the prefix-hit prefill, 32/8 heads, fp64 C oracle"}
     log(f"cpu stages: {json.dumps(out)}")
+    return out
+
+
+def cpu_one_thread(args, log):
+    """The oracle on one host thread for the small configurations: the whole tiny chain
+    (QK-Norm + RoPE of q and k, the scatter, case-1 prefill; 337 tokens at 16/8 heads), 2048
+    random (token, head) rows of the 0.6B varlen prefill and 8 sequences of the 0.6B decode
+    batch.  Inputs are generated on the host (untimed); only the oracle calls are timed."""
+    import oracle
+    import workloads as wl
+    prev = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        out = {}
+        w = wl.tiny_chain(args.seed)
+        s = w.shape
+        q0, k0, v0 = wl.qkv_views(s)
+        hq, hkv = s.num_q_heads, s.num_kv_heads
+        table = oracle.rope_table(s.max_position, 128, s.rope_theta)
+        t0 = time.perf_counter()
+        qb = oracle.round_bf16(oracle.rmsnorm_rope(w.qkv, hq, 128, w.gamma_q, s.eps, w.positions, table,
+                                                   col_offset=q0))
+        kb = oracle.round_bf16(oracle.rmsnorm_rope(w.qkv, hkv, 128, w.gamma_k, s.eps, w.positions, table,
+                                                   col_offset=k0))
+        vb = np.ascontiguousarray(w.qkv[:, v0:]).reshape(-1, hkv, 128)
+        kc = np.zeros((w.num_blocks * 256, hkv, 128), np.uint16)
+        vc = np.zeros_like(kc)
+        oracle.store_kvcache(kb, vb, kc, vc, w.slot_mapping)
+        oracle.attn_prefill(qb, kb, vb, w.cu_seqlens, w.cu_seqlens, hq, hkv)
+        dt = time.perf_counter() - t0
+        T = int(sum(w.lengths))
+        out["tiny_chain"] = {"value": round(T / dt, 1), "unit": "tokens/s", "s": round(dt, 4),
+                             "sample": f"whole chain, {T} tokens, {hq}/{hkv} heads"}
+
+        w2 = wl.varlen_prefill(args.seed)
+        s2 = w2.shape
+        q0, k0, v0 = wl.qkv_views(s2)
+        qkv = w2.qkv()
+        n2 = qkv.shape[0]
+        q = np.ascontiguousarray(qkv[:, q0:k0]).reshape(n2, s2.num_q_heads, 128)
+        k = np.ascontiguousarray(qkv[:, k0:v0]).reshape(n2, s2.num_kv_heads, 128)
+        v = np.ascontiguousarray(qkv[:, v0:]).reshape(n2, s2.num_kv_heads, 128)
+        rng = np.random.default_rng(args.seed + 300)
+        t = rng.integers(0, n2, 2048)
+        rows = np.stack([t, rng.integers(0, s2.num_q_heads, 2048)], 1)
+        t0 = time.perf_counter()
+        oracle.attn_prefill(q, k, v, w2.cu_seqlens, w2.cu_seqlens, s2.num_q_heads, s2.num_kv_heads, rows=rows)
+        dt = time.perf_counter() - t0
+        flop = float(np.sum(4 * 128 * (w2.positions[t] + 1)))
+        out["varlen_prefill_0_6b"] = {"value": round(flop / dt / 1e9, 4), "unit": "GFLOP/s", "s": round(dt, 4),
+                                      "sample": "2048 random (token, head) rows of the 8-sequence batch"}
+
+        w3 = wl.paged_decode_0_6b(args.seed)
+        s3 = w3.shape
+        seqs = list(range(8))
+        cl = w3.context_lens[seqs].astype(np.int32)
+        nblk = [-(-int(c) // 256) for c in cl]
+        rows_bt, nxt = [], 0
+        for nb in nblk:
+            rows_bt.append(list(range(nxt, nxt + nb)))
+            nxt += nb
+        bt = wl.pad_block_tables(rows_bt, w3.block_tables.shape[1])
+        rng = wl.rng_for(3, args.seed, 40)
+        kc = wl.normal_bf16(rng, (nxt * 256, s3.num_kv_heads, 128))
+        vc = wl.normal_bf16(rng, (nxt * 256, s3.num_kv_heads, 128))
+        qd = w3.q()[seqs]
+        t0 = time.perf_counter()
+        oracle.attn_decode(qd, kc, vc, cl, bt, s3.num_q_heads, s3.num_kv_heads)
+        dt = time.perf_counter() - t0
+        nbytes = int(np.sum(cl.astype(np.int64))) * s3.num_kv_heads * 128 * 4 + len(seqs) * s3.num_q_heads * 512
+        out["paged_decode_0_6b"] = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "s": round(dt, 4),
+                                    "sample": f"{len(seqs)} of the {w3.batch} sequences "
+                                              f"({int(cl.sum())} context tokens)"}
+        out.update({"cores": oracle.num_threads(), "kind": "oracle"})
+    finally:
+        oracle.set_num_threads(prev)
+    log(f"cpu one-thread: {json.dumps(out)}")
     return out
 
 

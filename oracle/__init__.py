@@ -66,6 +66,8 @@ def _load():
     lib.orc_attn_decode.restype = ctypes.c_int
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = ctypes.c_int
+    lib.orc_set_num_threads.argtypes = [I32]
+    lib.orc_set_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -80,6 +82,11 @@ def _c(a, dtype):
 
 def num_threads() -> int:
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> int:
+    """Host threads the following oracle calls use; returns the count in force."""
+    return int(_load().orc_set_num_threads(int(n)))
 
 
 # --------------------------------------------------------------------------

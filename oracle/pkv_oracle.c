@@ -344,3 +344,13 @@ ORC_EXPORT int orc_num_threads(void) {
     return 1;
 #endif
 }
+
+/* Threads the following oracle calls use (n > 0); returns the count now in force. */
+ORC_EXPORT int orc_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+    return orc_num_threads();
+}

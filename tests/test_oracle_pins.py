@@ -469,3 +469,37 @@ def test_tiny_chain_oracle_end_to_end():
         od = oracle.attn_decode(qd, kc, vc, st.context_lens, w.block_tables, s.num_q_heads, s.num_kv_heads)
         assert od.shape == (2, 16, 128)
         assert np.all(np.isfinite(od))
+
+
+def test_results_do_not_depend_on_the_thread_count():
+    """Each output row is computed by one thread with its own accumulators, so one host
+    thread and all of them give identical bits (prefill, decode and QK-Norm + RoPE)."""
+    w = wl.tiny_chain(seed=2)
+    s = w.shape
+    q0, k0, v0 = wl.qkv_views(s)
+    table = oracle.rope_table(4096, 128, s.rope_theta)
+    n = w.qkv.shape[0]
+    q = np.ascontiguousarray(w.qkv[:, q0:k0]).reshape(n, s.num_q_heads, 128)
+    k = np.ascontiguousarray(w.qkv[:, k0:v0]).reshape(n, s.num_kv_heads, 128)
+    v = np.ascontiguousarray(w.qkv[:, v0:]).reshape(n, s.num_kv_heads, 128)
+    kc = np.zeros((w.num_blocks * 256, s.num_kv_heads, 128), np.uint16)
+    vc = np.zeros_like(kc)
+    oracle.store_kvcache(k, v, kc, vc, w.slot_mapping)
+    ctx = np.array(w.lengths, np.int32)
+
+    def run():
+        return (oracle.attn_prefill(q, k, v, w.cu_seqlens, w.cu_seqlens, s.num_q_heads, s.num_kv_heads),
+                oracle.attn_decode(q[np.cumsum(w.lengths) - 1], kc, vc, ctx, w.block_tables, s.num_q_heads,
+                                   s.num_kv_heads),
+                oracle.rmsnorm_rope(w.qkv, s.num_q_heads, 128, w.gamma_q, s.eps, w.positions % 4096, table,
+                                    col_offset=q0))
+
+    prev = oracle.num_threads()
+    try:
+        assert oracle.set_num_threads(1) == 1
+        one = run()
+    finally:
+        oracle.set_num_threads(prev)
+    assert oracle.num_threads() == prev
+    for a, b in zip(one, run()):
+        assert np.array_equal(a, b)
