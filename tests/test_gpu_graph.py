@@ -62,12 +62,15 @@ class _Sequences:
         return qkv, pos.astype(np.int64), slots, ctx_i32
 
 
-@pytest.mark.parametrize("hq,hkv", [(32, 8), (16, 8)])
-def test_decode_graph_replays_match_eager_and_oracle(dev, hq, hkv):
+@pytest.mark.parametrize("hq,hkv,max_batch,max_ctx,batches", [
+    (32, 8, 32, 1000, [3, 32, 17, 1, 9, 5]),
+    (16, 8, 32, 1000, [3, 32, 17, 1, 9, 5]),
+    (32, 8, 512, 256, [512, 300, 257, 1, 129]),     # the whole ladder 1 ... 512, batches past a bucket edge
+])
+def test_decode_graph_replays_match_eager_and_oracle(dev, hq, hkv, max_batch, max_ctx, batches):
     shape = wl.QWEN3_8B if hq == 32 else wl.QWEN3_0_6B
-    max_batch, batches = 32, [3, 32, 17, 1, 9, 5]
     _say(f"decode graph {hq}/{hkv} heads, max_batch {max_batch}, batches {batches}")
-    seqs = _Sequences(max_batch, 1000, len(batches), seed=hq)
+    seqs = _Sequences(max_batch, max_ctx, len(batches), seed=hq + max_batch)
     rng = wl.rng_for(94, hq, 0)
     pool0 = wl.normal_bf16(rng, (2, seqs.num_blocks, 256, hkv, D))
     gq, gk = wl.gamma_bf16(rng), wl.gamma_bf16(rng)
@@ -89,7 +92,7 @@ def test_decode_graph_replays_match_eager_and_oracle(dev, hq, hkv):
     graph, gb = make()
     eager, eb = make()
     graph.capture()
-    assert graph.buckets == (1, 2, 4, 8, 16, 32)
+    assert graph.buckets == tuple(1 << i for i in range(max_batch.bit_length()))
     ek, ev = pool0[0].reshape(-1, hkv, D).copy(), pool0[1].reshape(-1, hkv, D).copy()
     q0, k0, v0 = wl.qkv_views(shape)
 
