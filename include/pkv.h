@@ -192,6 +192,13 @@ PKV_API int pkv_qk_norm_rope_store(const void* q, int64_t q_row_stride, const vo
  *   causal            must be 1 (the pages only use causal attention).
  * Sequences with Lq_b == 0 contribute nothing.  Output rows are written in
  * full for every query row.
+ *
+ * Large batches run as two kernels on `stream`: a fast pass, then a pass that
+ * recomputes any work item whose softmax sums left the fast pass's range (until
+ * then such rows of o hold a marker value, so o is complete only when the call's
+ * work on `stream` is).  The library keeps one 8-byte device word per GPU for
+ * this; calls on several streams may overlap, and a call may be captured into a
+ * HIP graph and replayed.
  */
 PKV_API int pkv_attn_prefill_varlen(const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride,
                             const void* v, int64_t v_row_stride, void* o, const int32_t* cu_seqlens_q,
