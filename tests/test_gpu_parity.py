@@ -451,6 +451,52 @@ def test_prefill_flagged_and_clean_calls_on_two_streams(dev):
             check_attn(got, ref, f"two streams, {first} first")
 
 
+def test_prefill_captured_in_a_graph(dev):
+    """Two-pass prefill calls captured into HIP graphs (one whose fast pass flags rows,
+    one clean) and replayed several times, with eager prefill calls and other work
+    between the replays: every replay gives the eager result byte for byte."""
+    _say("prefill: two-pass calls captured into graphs and replayed")
+    hq, hkv = 32, 8
+    lens_a, lens_b = [4096, 4096], [2048] * 4
+    rng = wl.rng_for(92, 78, 0)
+    qa, ka, va = _extreme_scores(hq, hkv, "large")(rng, sum(lens_a), sum(lens_a))
+    qb = wl.normal_bf16(rng, (sum(lens_b), hq, D))
+    kb = wl.normal_bf16(rng, (sum(lens_b), hkv, D))
+    vb = wl.normal_bf16(rng, (sum(lens_b), hkv, D))
+    cua, cub = wl.cu_seqlens(lens_a), wl.cu_seqlens(lens_b)
+    da = [to_dev(x, dev) for x in (qa, ka, va, cua)]
+    db = [to_dev(x, dev) for x in (qb, kb, vb, cub)]
+    ga, gb = torch.empty_like(da[0]), torch.empty_like(db[0])    # the graphs' outputs
+    ea = pkv.attn_prefill_varlen(da[0], da[1], da[2], da[3], da[3], 4096, 4096)
+    eb = pkv.attn_prefill_varlen(db[0], db[1], db[2], db[3], db[3], 2048, 2048)
+    torch.cuda.synchronize()
+    graphs = []
+    for d, o, L in ((da, ga, 4096), (db, gb, 2048)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):       # the binding enqueues on the capturing stream
+            pkv.attn_prefill_varlen(d[0], d[1], d[2], d[3], d[3], L, L, out=o)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        ga.fill_(0)
+        gb.fill_(0)
+        order = graphs if rep % 2 == 0 else graphs[::-1]
+        for g in order:
+            g.replay()
+        # eager work between replays: another flagged call and unrelated kernels
+        extra = pkv.attn_prefill_varlen(da[0], da[1], da[2], da[3], da[3], 4096, 4096)
+        junk = torch.randn(1 << 20, device=dev).sum()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        assert torch.equal(ga.view(torch.int16), ea.view(torch.int16)), f"replay {rep}: flagged call"
+        assert torch.equal(gb.view(torch.int16), eb.view(torch.int16)), f"replay {rep}: clean call"
+        assert torch.equal(extra.view(torch.int16), ea.view(torch.int16)), f"replay {rep}: eager call"
+    t = np.arange(0, sum(lens_a), 37)
+    rows = np.concatenate([np.stack([t, np.zeros_like(t)], 1), np.stack([t, np.full_like(t, hq - 1)], 1)])
+    ref = oracle.attn_prefill(qa, ka, va, cua, cua, hq, hkv, rows=rows)
+    check_attn(f64(ga)[rows[:, 0], rows[:, 1]], ref, "graph replay, flagged call")
+
+
 def test_prefill_paged_prefix(dev):
     lk, lq = [300, 513, 64, 1000], [40, 257, 64, 1]
     _say(f"prefill case 2 (paged), Lk {lk}, Lq {lq}")
