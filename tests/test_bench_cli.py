@@ -13,3 +13,39 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_recorded_traffic_follows_the_kernel_source(tmp_path, monkeypatch):
+    """The committed traffic figures resolve for the current kernel sources, and a
+    profile whose recorded source hash differs from the source gives null."""
+    sys.path.insert(0, ROOT)
+    import bench
+    for prof, src in (("attn_decode_paged_qwen3_8b_hbm_traffic.md", "attn_decode.hip"),
+                      ("attn_prefill_qwen3_8b_prefix_hbm_traffic.md", "attn_prefill.hip")):
+        v = bench.recorded_traffic(prof, src)
+        assert isinstance(v, int) and v > 0, f"{prof} does not match {src}: profile it again"
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "paged_kv_gqa_amd" / "csrc").mkdir(parents=True)
+    (tmp_path / "paged_kv_gqa_amd" / "csrc" / "k.hip").write_text("kernel source\n")
+    (tmp_path / "profiles" / "p.md").write_text("traffic_bytes_per_launch: 123\nsource_sha256: " + "0" * 64 + "\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.recorded_traffic("p.md", "k.hip") is None
+    assert bench.recorded_traffic("missing.md", "k.hip") is None
+
+
+def test_input_checksum_sees_every_word():
+    """The checksum recorded beside the seed changes when any one input word changes,
+    and not when nothing does."""
+    import torch
+    sys.path.insert(0, ROOT)
+    import bench
+    a = torch.arange(1 << 12, dtype=torch.int32).view(torch.bfloat16)
+    b = torch.arange(100, dtype=torch.int64)
+    ref = bench.input_checksum(torch, [("a", a), ("b", b)])
+    assert ref == bench.input_checksum(torch, [("a", a.clone()), ("b", b.clone())])
+    for i in (0, 1234, a.numel() - 1):
+        a2 = a.clone()
+        a2.view(torch.int16)[i] += 1
+        assert bench.input_checksum(torch, [("a", a2), ("b", b)]) != ref
+    assert bench.input_checksum(torch, [("a", a), ("b", b + 1)]) != ref
+    assert bench.input_checksum(torch, [("b", b), ("a", a)]) != ref
