@@ -56,13 +56,14 @@ def _load():
     lib.orc_bf16_to_double.restype = None
     lib.orc_rope_table.argtypes = [P, I32, I32, F64]
     lib.orc_rope_table.restype = ctypes.c_int
-    lib.orc_rmsnorm_rope.argtypes = [P, I64, I32, I32, I32, P, F64, P, P, I32, P]
+    lib.orc_rmsnorm_rope.argtypes = [P, I64, I32, I32, I32, P, F64, P, P, I32, I32, P]
     lib.orc_rmsnorm_rope.restype = ctypes.c_int
     lib.orc_store_kvcache.argtypes = [P, I64, P, I64, P, P, I64, P, I32, I32, I32]
     lib.orc_store_kvcache.restype = ctypes.c_int
-    lib.orc_attn_prefill.argtypes = [P, I64, P, I64, P, I64, P, P, I32, I32, I32, I32, F64, P, I32, I32, P, I64, P]
+    lib.orc_attn_prefill.argtypes = [P, I64, P, I64, P, I64, P, P, I32, I32, I32, I32, F64, P, I32, I32, I64, P, I64,
+                                     P]
     lib.orc_attn_prefill.restype = ctypes.c_int
-    lib.orc_attn_decode.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, F64, P, I32, P]
+    lib.orc_attn_decode.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, I64, F64, P, I32, P]
     lib.orc_attn_decode.restype = ctypes.c_int
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = ctypes.c_int
@@ -127,24 +128,32 @@ def rope_table(max_pos: int = 40960, rot_dim: int = 128, theta: float = 1.0e6) -
 
 def rmsnorm_rope(x: np.ndarray, n_heads: int, head_dim: int, gamma: np.ndarray, eps: float,
                  positions: np.ndarray, table: np.ndarray, row_stride: Optional[int] = None,
-                 col_offset: int = 0) -> np.ndarray:
+                 col_offset: int = 0, pages_rounding: bool = False) -> np.ndarray:
     """Per-head RMSNorm (QK-Norm) then RoPE, unrounded fp64 [N, n_heads, head_dim].
 
     x is a bf16 2-D array of rows; the heads start at column ``col_offset``.
     "3.3 Model skeleton and core operators", sections 2, 3 and 8;
     "Nano-vLLM 源码解读 #17 注意力层", section 4.
+
+    ``pages_rounding``: round to bf16 at the three places the pages' code holds a
+    bf16 tensor -- the normalised row (cast back before the weight multiply,
+    section 2), its product with gamma, and the rotated row (cast to the input
+    dtype, section 3) -- instead of leaving the result unrounded.
     """
     x = _c(x, np.uint16)
     assert x.ndim == 2
     n = x.shape[0]
     rs = x.shape[1] if row_stride is None else row_stride
+    if col_offset < 0 or col_offset + n_heads * head_dim > rs or (n and rs * (n - 1) + col_offset +
+                                                                 n_heads * head_dim > x.size):
+        raise ValueError("heads outside the rows of x")
     pos = _c(positions, np.int64)
     tab = _c(table, np.float32)
     g = _c(gamma, np.uint16)
     out = np.empty((n, n_heads, head_dim), dtype=np.float64)
     base = x.ctypes.data + 2 * col_offset
     rc = _load().orc_rmsnorm_rope(ctypes.c_void_p(base), rs, n, n_heads, head_dim, _p(g), float(eps),
-                                  _p(pos), _p(tab), tab.shape[0], _p(out))
+                                  _p(pos), _p(tab), tab.shape[0], int(bool(pages_rounding)), _p(out))
     if rc:
         raise ValueError(f"orc_rmsnorm_rope rejected its arguments ({rc})")
     return out
@@ -200,16 +209,29 @@ def attn_prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens_q: np.n
     table (case 2).  "3.3 Model skeleton and core operators", section 7.2;
     "nano-vllm code walkthrough", "Prefill stage"; "同一个 Qwen3，两种写法", s3.2.
     Returns [Tq, Hq, d] (or [n_rows, d] when ``rows`` lists (t, h) pairs).
+    Raises ValueError when a key a query attends does not exist: a block id
+    outside the pool (or -1) among a sequence's first ceil(Lk / block_size)
+    table entries, or contiguous key rows past the end of k/v.
     """
     q = _c(q, np.uint16)
     k = _c(k, np.uint16)
     v = _c(v, np.uint16)
+    if block_table is not None and k.ndim == 4:      # caches given as [num_blocks, block_size, Hkv, d]
+        k = k.reshape(-1, k.shape[2], k.shape[3])
+        v = v.reshape(-1, v.shape[2], v.shape[3])
     qs = q_row_stride if q_row_stride is not None else int(np.prod(q.shape[1:]))
     ks = k_row_stride if k_row_stride is not None else int(np.prod(k.shape[1:]))
     vs = v_row_stride if v_row_stride is not None else int(np.prod(v.shape[1:]))
     cq = _c(cu_seqlens_q, np.int32)
     ck = _c(cu_seqlens_k, np.int32)
     B = cq.shape[0] - 1
+    if ck.shape[0] != B + 1 or int(cq[-1]) > q.shape[0]:
+        raise ValueError("cu_seqlens do not match the inputs")
+    for arr, col, stride, heads in ((q, q_col, qs, num_q_heads), (k, k_col, ks, num_kv_heads),
+                                    (v, v_col, vs, num_kv_heads)):
+        if col < 0 or col + heads * head_dim > stride or stride * max(arr.shape[0] - 1, 0) + col + \
+                heads * head_dim > max(arr.size, 1):
+            raise ValueError("heads outside the rows of an input")
     sc = head_dim ** -0.5 if scale is None else scale
     bt = None if block_table is None else _c(block_table, np.int32)
     mb = 0 if bt is None else bt.shape[1]
@@ -220,11 +242,15 @@ def attn_prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens_q: np.n
         rows = _c(rows, np.int64).reshape(-1, 2)
         out = np.empty((rows.shape[0], head_dim), dtype=np.float64)
         rp, nr = rows, rows.shape[0]
+    n_slots = min(k.shape[0], v.shape[0])
     rc = _load().orc_attn_prefill(ctypes.c_void_p(q.ctypes.data + 2 * q_col), qs,
                                   ctypes.c_void_p(k.ctypes.data + 2 * k_col), ks,
                                   ctypes.c_void_p(v.ctypes.data + 2 * v_col), vs, _p(cq), _p(ck), B,
                                   num_q_heads, num_kv_heads, head_dim, float(sc), _p(bt), mb, block_size,
-                                  _p(rp), nr, _p(out))
+                                  n_slots, _p(rp), nr, _p(out))
+    if rc == -3:
+        raise ValueError("orc_attn_prefill: a sequence attends keys that do not exist (block id outside the "
+                         "pool, -1, or rows past the end of k/v)")
     if rc:
         raise ValueError(f"orc_attn_prefill rejected its arguments ({rc})")
     return out
@@ -238,6 +264,9 @@ def attn_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, context
 
     "3.3 Model skeleton and core operators", section 7.2;
     "nano-vllm code walkthrough", "Decode Stage".
+    The caches are arrays of slot rows ([num_slots, Hkv, d] or any shape that
+    flattens to it).  Raises ValueError when a block id among a sequence's first
+    ceil(context_len / block_size) table entries is -1 or outside the pool.
     """
     q = _c(q, np.uint16)
     kc = k_cache if (k_cache.flags.c_contiguous and k_cache.dtype == np.uint16) else _c(k_cache, np.uint16)
@@ -252,8 +281,13 @@ def attn_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, context
         sp = _c(seqs, np.int32)
         ns, nout = sp.shape[0], sp.shape[0]
     out = np.empty((nout, num_q_heads, head_dim), dtype=np.float64)
+    if bt.ndim != 2 or bt.shape[0] != B or q.size < B * num_q_heads * head_dim:
+        raise ValueError("block_table / q do not match context_lens")
+    n_slots = min(kc.size, vc.size) // (num_kv_heads * head_dim)
     rc = _load().orc_attn_decode(_p(q), _p(kc), _p(vc), _p(cl), _p(bt), bt.shape[1], B, num_q_heads,
-                                 num_kv_heads, head_dim, block_size, float(sc), _p(sp), ns, _p(out))
+                                 num_kv_heads, head_dim, block_size, n_slots, float(sc), _p(sp), ns, _p(out))
+    if rc == -3:
+        raise ValueError("orc_attn_decode: a context reaches a block id that is -1 or outside the pool")
     if rc:
         raise ValueError(f"orc_attn_decode rejected its arguments ({rc})")
     return out

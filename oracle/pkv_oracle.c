@@ -118,11 +118,16 @@ ORC_EXPORT int orc_rope_table(float* out, int32_t max_pos, int32_t rot_dim, doub
 /*   x  : bf16 [n_tokens] rows, row_stride elements apart, heads of d at     */
 /*        head stride d inside a row                                         */
 /*   out: double [n_tokens][n_heads][d], unrounded                           */
+/*   pages_rounding != 0: round to bf16 where the pages' code holds bf16     */
+/*        tensors -- after normalising, after the product with gamma ([P1]   */
+/*        s2: the row is cast back before the weight multiply) and after the */
+/*        rotation ([P1] s3 / [P4] s3.5: the rotated row is cast to x's      */
+/*        dtype); out then holds those bf16 values.                          */
 /* ------------------------------------------------------------------------ */
 
 ORC_EXPORT int orc_rmsnorm_rope(const uint16_t* x, int64_t row_stride, int32_t n_tokens, int32_t n_heads,
                                 int32_t d, const uint16_t* gamma, double eps, const int64_t* positions,
-                                const float* table, int32_t max_pos, double* out) {
+                                const float* table, int32_t max_pos, int32_t pages_rounding, double* out) {
     if (d <= 0 || d > 512 || (d & 1) || n_tokens < 0 || n_heads <= 0) return -1;
     int half = d / 2;
     for (int32_t t = 0; t < n_tokens; ++t)
@@ -135,7 +140,14 @@ ORC_EXPORT int orc_rmsnorm_rope(const uint16_t* x, int64_t row_stride, int32_t n
             double ss = 0.0;
             for (int i = 0; i < d; ++i) { double v = bf16_val(xr[i]); ss += v * v; }
             double r = 1.0 / sqrt(ss / (double)d + eps);
-            for (int i = 0; i < d; ++i) y[i] = bf16_val(xr[i]) * r * bf16_val(gamma[i]);
+            if (pages_rounding) {
+                /* the pages' precision steps: the normalised row is cast to bf16,
+                   multiplied by gamma in bf16 (one rounding of the exact product) */
+                for (int i = 0; i < d; ++i)
+                    y[i] = bf16_val(bf16_rne(bf16_val(bf16_rne(bf16_val(xr[i]) * r)) * bf16_val(gamma[i])));
+            } else {
+                for (int i = 0; i < d; ++i) y[i] = bf16_val(xr[i]) * r * bf16_val(gamma[i]);
+            }
             const float* cs = table + positions[t] * (int64_t)d;
             double* o = out + ((int64_t)t * n_heads + h) * d;
             for (int i = 0; i < half; ++i) {
@@ -143,6 +155,10 @@ ORC_EXPORT int orc_rmsnorm_rope(const uint16_t* x, int64_t row_stride, int32_t n
                 double x1 = y[i], x2 = y[half + i];
                 o[i] = x1 * c - x2 * s;
                 o[half + i] = x2 * c + x1 * s;
+                if (pages_rounding) {   /* the rotated row is cast back to bf16 */
+                    o[i] = bf16_val(bf16_rne(o[i]));
+                    o[half + i] = bf16_val(bf16_rne(o[half + i]));
+                }
             }
         }
     }
@@ -238,6 +254,25 @@ static void attn_row(const double* q, const key_src* src, int64_t n_keys, double
 /*   work to those outputs (n_rows < 0: all rows).                            */
 /* ------------------------------------------------------------------------ */
 
+/* Every key a sequence attends must exist: in the paged case its block id is
+ * in [0, num_slots / block_size) for each of the first ceil(n_keys / bs) table
+ * entries (and the table is wide enough); in the contiguous case its rows lie
+ * inside the num_slots rows given.  The pages never define what an unusable id
+ * means (the kernels drop such keys); the oracle refuses the input instead, so a
+ * test cannot read outside the host arrays by accident.  Returns 0 or -3. */
+static int check_keys(const int32_t* bt_row, int32_t max_blocks, int32_t block_size, int64_t row0,
+                      int64_t n_keys, int64_t num_slots) {
+    if (n_keys <= 0) return 0;
+    if (!bt_row) return (row0 >= 0 && row0 + n_keys <= num_slots) ? 0 : -3;
+    if (block_size <= 0) return -3;
+    int64_t nblk = (n_keys + block_size - 1) / block_size;
+    if (nblk > max_blocks) return -3;
+    int64_t pool = num_slots / block_size;
+    for (int64_t i = 0; i < nblk; ++i)
+        if (bt_row[i] < 0 || (int64_t)bt_row[i] >= pool) return -3;
+    return 0;
+}
+
 static int find_seq(const int32_t* cu, int32_t nseq, int64_t t) {
     int lo = 0, hi = nseq - 1;
     while (lo < hi) {            /* last b with cu[b] <= t */
@@ -251,16 +286,22 @@ ORC_EXPORT int orc_attn_prefill(const uint16_t* q, int64_t q_row_stride, const u
                                 const uint16_t* v, int64_t v_row_stride, const int32_t* cu_q, const int32_t* cu_k,
                                 int32_t num_seqs, int32_t hq, int32_t hkv, int32_t d, double scale,
                                 const int32_t* block_table, int32_t max_blocks, int32_t block_size,
-                                const int64_t* rows, int64_t n_rows, double* out) {
+                                int64_t num_slots, const int64_t* rows, int64_t n_rows, double* out) {
     if (num_seqs <= 0 || hq <= 0 || hkv <= 0 || hq % hkv || d <= 0 || d > 512) return -1;
     int32_t group = hq / hkv;
     int64_t Tq = cu_q[num_seqs];
     int64_t maxk = 0;
+    if (cu_q[0] != 0) return -2;
     for (int b = 0; b < num_seqs; ++b) {
         int64_t lq = cu_q[b + 1] - cu_q[b], lk = cu_k[b + 1] - cu_k[b];
         if (lq < 0 || lk < lq) return -2;
         if (lk > maxk) maxk = lk;
+        if (check_keys(block_table ? block_table + (int64_t)b * max_blocks : NULL, max_blocks, block_size,
+                       cu_k[b], lk, num_slots))
+            return -3;
     }
+    for (int64_t r = 0; n_rows >= 0 && r < n_rows; ++r)
+        if (rows[2 * r] < 0 || rows[2 * r] >= Tq || rows[2 * r + 1] < 0 || rows[2 * r + 1] >= hq) return -4;
     int64_t total = n_rows < 0 ? Tq * hq : n_rows;
 #pragma omp parallel
     {
@@ -301,14 +342,18 @@ ORC_EXPORT int orc_attn_prefill(const uint16_t* q, int64_t q_row_stride, const u
 ORC_EXPORT int orc_attn_decode(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
                                const int32_t* context_lens, const int32_t* block_table, int32_t max_blocks,
                                int32_t num_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t block_size,
-                               double scale, const int32_t* seqs, int32_t n_sel, double* out) {
+                               int64_t num_slots, double scale, const int32_t* seqs, int32_t n_sel, double* out) {
     if (num_seqs < 0 || hq <= 0 || hkv <= 0 || hq % hkv || d <= 0 || d > 512) return -1;
     int32_t group = hq / hkv;
     int32_t nsel = n_sel < 0 ? num_seqs : n_sel;
     int64_t maxk = 1;
     for (int32_t s = 0; s < nsel; ++s) {
         int32_t b = n_sel < 0 ? s : seqs[s];
+        if (b < 0 || b >= num_seqs) return -4;
+        if (context_lens[b] < 0) return -2;
         if (context_lens[b] > maxk) maxk = context_lens[b];
+        if (check_keys(block_table + (int64_t)b * max_blocks, max_blocks, block_size, 0, context_lens[b], num_slots))
+            return -3;
     }
     int64_t row_stride = (int64_t)hkv * d;
 #pragma omp parallel

@@ -195,6 +195,88 @@ def test_rope_relative_position_property():
     assert abs(dot(7, 3) - dot(7, 5)) > 1e-3       # and it does depend on the offset
 
 
+def test_pages_rounding_worked_example():
+    """Pages-rounding mode rounds the normalised row to bf16, then its product with gamma,
+    then the rotated row.  Worked by hand for x = [3, 1, 1, ..., 1] at position 0 (no
+    rotation), gamma_0 = 1 + 2^-7: mean square (9 + 127) / 128 = 1.0625, so
+    n_0 = 3 / sqrt(1.0625 + 1e-6) = 2.91043..., which rounds (bf16 steps of 2^-6 in [2, 4))
+    to 186 * 2^-6 = 2.90625; 2.90625 * (1 + 2^-7) = 2.92896 rounds to 187 * 2^-6 = 2.921875.
+    Rounded once instead, 2.91043 * (1 + 2^-7) = 2.93317 -> 188 * 2^-6 = 2.9375: the two
+    pipelines differ here by one bf16 step.  The other elements: n = 0.97014 -> 0.96875
+    (248 * 2^-8), times gamma 1 stays 0.96875."""
+    x = np.ones(D, np.float32)
+    x[0] = 3.0
+    g = np.ones(D, np.float32)
+    g[0] = 1.0 + 2.0 ** -7
+    xb = wl.bf16_bits(x.reshape(1, -1))
+    gb = wl.bf16_bits(g)
+    tab = oracle.rope_table(4, D, 1e6)
+    pages = oracle.rmsnorm_rope(xb, 1, D, gb, 1e-6, np.array([0]), tab, pages_rounding=True)[0, 0]
+    once = oracle.rmsnorm_rope(xb, 1, D, gb, 1e-6, np.array([0]), tab)[0, 0]
+    assert pages[0] == 2.921875
+    assert np.all(pages[1:] == 0.96875)
+    assert once[0] == pytest.approx(3.0 / math.sqrt(1.0625 + 1e-6) * (1 + 2.0 ** -7), rel=1e-14)
+    assert wl.bf16_to_f32(oracle.round_bf16(once[:1]))[0] == 2.9375
+    # constant input with gamma 1.5: n = 1/sqrt(1 + 1e-6) rounds to 1.0, so y = 1.5 exactly
+    c = oracle.rmsnorm_rope(wl.bf16_bits(np.ones((1, D), np.float32)), 1, D,
+                            wl.bf16_bits(np.full(D, 1.5, np.float32)), 1e-6, np.array([0]), tab,
+                            pages_rounding=True)[0, 0]
+    assert np.all(c == 1.5)
+
+
+def _pages_torch_code(x_bits, n_heads, gamma_bits, eps, positions, table):
+    """The pages' own code, run with torch on the CPU: rms_forward ("3.3 Model skeleton and
+    core operators" section 2) then apply_rotary_emb (section 3) with the fp32 table."""
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).reshape(x_bits.shape[0], n_heads, D)
+    w = torch.from_numpy(gamma_bits.view(np.int16)).view(torch.bfloat16)
+    xf = x.float()
+    var = xf.pow(2).mean(dim=-1, keepdim=True)
+    xf.mul_(torch.rsqrt(var + eps))
+    y = xf.to(torch.bfloat16).mul_(w)
+    cos, sin = torch.from_numpy(table[positions]).unsqueeze(1).chunk(2, dim=-1)
+    x1, x2 = torch.chunk(y.float(), 2, dim=-1)
+    out = torch.cat((x1 * cos - x2 * sin, x2 * cos + x1 * sin), dim=-1).to(torch.bfloat16)
+    return out.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_pages_rounding_matches_the_pages_torch_code():
+    """The pages compute the mean square, the root and the rotation in fp32, the oracle in
+    fp64; the bf16 results agree except where an fp32 rounding moves a value across a bf16
+    rounding boundary (then by one bf16 step)."""
+    rng = np.random.default_rng(12)
+    n, heads = 400, 8
+    x = wl.bf16_bits((2.5 * rng.standard_normal((n, heads * D))).astype(np.float32))
+    g = wl.bf16_bits(1 + 0.05 * rng.standard_normal(D).astype(np.float32))
+    pos = rng.integers(0, 40960, n)
+    tab = oracle.rope_table(40960, D, 1e6)
+    ref = _pages_torch_code(x, heads, g, 1e-6, pos, tab)
+    got = oracle.rmsnorm_rope(x, heads, D, g, 1e-6, pos, tab, pages_rounding=True)
+    got_bits = oracle.round_bf16(got)
+    np.testing.assert_array_equal(wl.bf16_to_f32(got_bits).astype(np.float64), got)   # already bf16 values
+    ref = ref.reshape(got_bits.shape)
+    same = np.mean(got_bits == ref)
+    assert same >= 0.999, same
+    # Where they differ, an fp32 rounding moved a value across a bf16 boundary: the
+    # normalised row or its product with gamma by one bf16 step (at most one step of the
+    # rotated pair's length after the rotation, |cos|, |sin| <= 1), or the result itself
+    # by one step; where x1 cos - x2 sin cancels far below its terms, the fp32 rotation's
+    # own error (a few 2^-24 of the pair's length) adds to that.
+    def step(a):
+        return np.exp2(np.floor(np.log2(np.maximum(np.abs(a), 2.0 ** -126))) - 7)
+    r = wl.bf16_to_f32(ref).astype(np.float64)
+    pair = np.sqrt(got[..., :64] ** 2 + got[..., 64:] ** 2)
+    pair = np.concatenate([pair, pair], axis=-1)
+    assert np.all(np.abs(got - r) <= step(r) + 2 * step(pair) + 2.0 ** -19 * pair)
+    # At position 0 (no rotation) the output is the bf16 product with gamma itself:
+    # differences are single bf16 steps.
+    z = np.zeros(n, np.int64)
+    ref0 = _pages_torch_code(x, heads, g, 1e-6, z, tab).reshape(got_bits.shape)
+    got0 = oracle.round_bf16(oracle.rmsnorm_rope(x, heads, D, g, 1e-6, z, tab, pages_rounding=True))
+    assert np.mean(got0 == ref0) >= 0.999
+    r0 = wl.bf16_to_f32(ref0).astype(np.float64)
+    assert np.all(np.abs(wl.bf16_to_f32(got0).astype(np.float64) - r0) <= step(r0))
+
+
 # ---------------------------------------------------------------------------
 # store_kvcache scatter
 # ---------------------------------------------------------------------------
