@@ -271,8 +271,8 @@ def main():
 
     cpu = cpu_pre = cpu_st = cpu_one = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args, wd, kc_d, vc_d, qo_d, log)
-        cpu_pre = cpu_baseline_prefill(args, wp, kc_p, vc_p, qo_p, log)
+        cpu = cpu_baseline(args, wd, kc_d, vc_d, qo_d, o_d, log)
+        cpu_pre = cpu_baseline_prefill(args, wp, kc_p, vc_p, qo_p, o_p, log)
         cpu_st = cpu_stages(args, wp, qkv_p, log)
         cpu_one = cpu_one_thread(args, log)
 
@@ -309,6 +309,9 @@ def main():
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "cpu_baseline": cpu,
+        "parity": ({"attn_decode_paged": cpu["parity"], "attn_prefill_varlen": cpu_pre["parity"],
+                    "reference": "fp64 CPU oracle on the inputs and outputs of the timed steps"}
+                   if cpu is not None and cpu_pre is not None else None),
         "sublayer_ops": ops,
         "qk_norm_rope_small": norm_small,
         "qwen3_0_6b": small,
@@ -642,7 +645,7 @@ def cpu_one_thread(args, log):
     return out
 
 
-def cpu_baseline(args, wd, kc_d, vc_d, q_d, log):
+def cpu_baseline(args, wd, kc_d, vc_d, q_d, o_d, log):
     """The oracle's paged decode over the decode workload's sequences, on the host cores.
 
     Sequences are copied back and run in groups of 32 so host memory stays bounded;
@@ -669,28 +672,43 @@ def cpu_baseline(args, wd, kc_d, vc_d, q_d, log):
     n = min(args.cpu_seqs, wd.batch)
     seqs_all = list(range(n))
     qh = bits(q_d)
+    got = bits(o_d).astype(np.uint32) << 16
+    got = got.view(np.float32).astype(np.float64)
     hq, hkv = wd.shape.num_q_heads, wd.shape.num_kv_heads
-    total, nbytes, toks = 0.0, 0, 0
+    total, logical, toks = 0.0, 0, 0
+    err_max, err_sum, err_n = 0.0, 0.0, 0
     for s0 in range(0, n, 32):
         seqs = seqs_all[s0:s0 + 32]
         kc, vc, bt = gather_sequences(seqs)
         cl = wd.context_lens[seqs]
         t0 = time.perf_counter()
-        oracle.attn_decode(qh[seqs], kc, vc, cl, bt, hq, hkv)
+        ref = oracle.attn_decode(qh[seqs], kc, vc, cl, bt, hq, hkv)
         total += time.perf_counter() - t0
+        err = np.abs(got[seqs] - ref)
+        err_max, err_sum, err_n = max(err_max, float(err.max())), err_sum + float(err.sum()), err_n + err.size
         toks += int(np.sum(cl.astype(np.int64)))
-        nbytes += int(np.sum(cl.astype(np.int64))) * hkv * 128 * 2 * 2 + len(seqs) * hq * 128 * 2 * 2
+        logical += int(np.sum(cl.astype(np.int64))) * hkv * 128 * 2 * 2 + len(seqs) * hq * 128 * 2 * 2
         del kc, vc
-    log(f"cpu baseline: {n} sequences, {nbytes / 1e9:.3f} GB in {total:.2f} s")
+    # the same algorithmic bytes as the GPU figure (shared prefix once) when the whole batch ran
+    unique = wd.algorithmic_bytes(unique=True) if n == wd.batch else None
+    nbytes = unique if unique is not None else logical
+    log(f"cpu baseline: {n} sequences, {nbytes / 1e9:.3f} GB in {total:.2f} s; GPU vs oracle max |err| "
+        f"{err_max:.3e} mean {err_sum / err_n:.3e}")
+    parity = {"max_abs": err_max, "mean_abs": err_sum / err_n, "compared": f"all {hq} heads of {n} sequences",
+              "gate": {"max_abs": 2e-2, "mean_abs": 2e-3},
+              "pass": bool(err_max <= 2e-2 and err_sum / err_n <= 2e-3)}
     return {"value": round(nbytes / total / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "cpu_model": cpu_model(),
+            "cpu_model": cpu_model(), "logical_GB/s": round(logical / total / 1e9, 4),
             "sample": f"paged decode of {n} of the {wd.batch} sequences ({toks} context tokens, {hq}/{hkv} heads), "
-                      f"fp64 C oracle with OpenMP, {total:.2f} s of oracle time (K/V read per sequence, "
-                      f"shared prefix counted per sequence)"}
+                      f"fp64 C oracle with OpenMP, {total:.2f} s of oracle time; value in the GPU figure's bytes "
+                      f"({'shared prefix counted once' if unique is not None else 'K/V per sequence'}), "
+                      f"logical_GB/s with the prefix counted per sequence as the oracle reads it",
+            "parity": parity}
 
 
-def cpu_baseline_prefill(args, wp, kc_p, vc_p, q_p, log):
-    """The oracle's paged prefill on a sample of (token, head) rows of the prefill workload."""
+def cpu_baseline_prefill(args, wp, kc_p, vc_p, q_p, o_p, log):
+    """The oracle's paged prefill on a sample of (token, head) rows of the prefill workload,
+    compared with the same rows of the output the GPU produced in the timed steps."""
     import torch
 
     import oracle
@@ -706,13 +724,21 @@ def cpu_baseline_prefill(args, wp, kc_p, vc_p, q_p, log):
     kc, vc = bits(kc_p).reshape(-1, 8, 128), bits(vc_p).reshape(-1, 8, 128)
     qh = bits(q_p)
     t0 = time.perf_counter()
-    oracle.attn_prefill(qh, kc, vc, wp.cu_seqlens_q, wp.cu_seqlens_k, wp.shape.num_q_heads, wp.shape.num_kv_heads,
-                        block_table=wp.block_tables, rows=rows)
+    ref = oracle.attn_prefill(qh, kc, vc, wp.cu_seqlens_q, wp.cu_seqlens_k, wp.shape.num_q_heads,
+                              wp.shape.num_kv_heads, block_table=wp.block_tables, rows=rows)
     dt = time.perf_counter() - t0
+    got = (bits(o_p)[t, h].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    err = np.abs(got - ref)
     flop = float(np.sum(4 * 128 * (wp.positions[t] + 1)))
-    log(f"cpu prefill baseline: {nrows} rows, {flop / 1e9:.2f} GFLOP in {dt:.2f} s")
+    log(f"cpu prefill baseline: {nrows} rows, {flop / 1e9:.2f} GFLOP in {dt:.2f} s; GPU vs oracle max |err| "
+        f"{err.max():.3e} mean {err.mean():.3e}")
+    parity = {"max_abs": float(err.max()), "mean_abs": float(err.mean()),
+              "compared": f"{nrows} random (token, head) rows of {wp.num_q_tokens * wp.shape.num_q_heads}",
+              "gate": {"max_abs": 2e-2, "mean_abs": 2e-3},
+              "pass": bool(err.max() <= 2e-2 and err.mean() <= 2e-3)}
     return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{nrows} random (token, head) rows of the prefix-hit prefill, fp64 C oracle, {dt:.2f} s"}
+            "sample": f"{nrows} random (token, head) rows of the prefix-hit prefill, fp64 C oracle, {dt:.2f} s",
+            "parity": parity}
 
 
 if __name__ == "__main__":

@@ -161,6 +161,37 @@ def _i32(t, name):
     return t
 
 
+def _same_device(ref, **named):
+    """Every tensor given must live on the GPU that holds ``ref`` (the kernels get raw pointers)."""
+    if ref.device.type != "cuda":
+        raise ValueError(f"inputs must be GPU tensors, got {ref.device}")
+    for name, t in named.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, the inputs on {ref.device}")
+
+
+def _out(t, shape, ref, name):
+    """A caller-supplied output must be exactly the contiguous bf16 tensor the kernel writes."""
+    import torch
+    if t.dtype != torch.bfloat16 or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bfloat16 tensor of shape {tuple(shape)}, got "
+                         f"{t.dtype} {tuple(t.shape)}{'' if t.is_contiguous() else ' (not contiguous)'}")
+    if t.device != ref.device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {ref.device}")
+    return t
+
+
+def _norm_params(q_norm_weight, k_norm_weight, cos_sin_cache, ref):
+    import torch
+    for name, w in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
+        if w.dtype != torch.bfloat16 or w.numel() != HEAD_DIM or not w.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor of {HEAD_DIM} elements")
+    if cos_sin_cache.dtype != torch.float32 or cos_sin_cache.dim() != 2 or cos_sin_cache.shape[1] != HEAD_DIM \
+            or not cos_sin_cache.is_contiguous():
+        raise ValueError(f"cos_sin_cache must be a contiguous float32 [max_position, {HEAD_DIM}] table")
+    _same_device(ref, q_norm_weight=q_norm_weight, k_norm_weight=k_norm_weight, cos_sin_cache=cos_sin_cache)
+
+
 # ---------------------------------------------------------------------------
 # entry points
 # ---------------------------------------------------------------------------
@@ -192,12 +223,14 @@ def qk_norm_rope(q, k, positions, q_norm_weight, k_norm_weight, cos_sin_cache, e
         raise ValueError("q, k and positions must have the same number of tokens")
     if positions.dtype != torch.int64 or not positions.is_contiguous():
         raise TypeError("positions must be a contiguous int64 tensor")
+    _same_device(q, k=k, positions=positions)
+    _norm_params(q_norm_weight, k_norm_weight, cos_sin_cache, q)
     if q_out is None:
         q_out = torch.empty((n, hq, HEAD_DIM), dtype=torch.bfloat16, device=q.device)
     if k_out is None:
         k_out = torch.empty((n, hkv, HEAD_DIM), dtype=torch.bfloat16, device=k.device)
-    if not (q_out.is_contiguous() and k_out.is_contiguous()):
-        raise ValueError("q_out and k_out must be contiguous")
+    _out(q_out, (n, hq, HEAD_DIM), q, "q_out")
+    _out(k_out, (n, hkv, HEAD_DIM), q, "k_out")
     _check("pkv_qk_norm_rope",
            lib.pkv_qk_norm_rope(_ptr(q), qs, _ptr(k), ks, _ptr(q_out), _ptr(k_out), _ptr(positions), n, hq, hkv,
                                 HEAD_DIM, _ptr(q_norm_weight), _ptr(k_norm_weight), float(eps),
@@ -227,10 +260,15 @@ def qk_norm_rope_store(q, k, v, positions, q_norm_weight, k_norm_weight, cos_sin
     for c in (k_cache, v_cache):
         if c.dtype != torch.bfloat16 or not c.is_contiguous() or c.dim() != 4 or c.stride(1) != D:
             raise ValueError("caches must be contiguous bf16 [num_blocks, block_size, Hkv, 128]")
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    _same_device(q, k=k, v=v, positions=positions, slot_mapping=slot_mapping, k_cache=k_cache, v_cache=v_cache)
+    _norm_params(q_norm_weight, k_norm_weight, cos_sin_cache, q)
     if q_out is None:
         q_out = torch.empty((n, hq, HEAD_DIM), dtype=torch.bfloat16, device=q.device)
-    if not q_out.is_contiguous() or (k_out is not None and not k_out.is_contiguous()):
-        raise ValueError("q_out and k_out must be contiguous")
+    _out(q_out, (n, hq, HEAD_DIM), q, "q_out")
+    if k_out is not None:
+        _out(k_out, (n, hkv, HEAD_DIM), q, "k_out")
     _check("pkv_qk_norm_rope_store",
            lib.pkv_qk_norm_rope_store(_ptr(q), qs, _ptr(k), ks, _ptr(v), vs, _ptr(q_out), _ptr(k_out),
                                       _ptr(k_cache), _ptr(v_cache), k_cache.numel() // D, _ptr(slot_mapping),
@@ -248,9 +286,13 @@ def store_kvcache(key, value, k_cache, v_cache, slot_mapping, stream=None):
     D = hkv * HEAD_DIM
     if k_cache.stride(1) != D or v_cache.stride(1) != D or not (k_cache.is_contiguous() and v_cache.is_contiguous()):
         raise ValueError("caches must be contiguous with stride(1) == num_kv_heads*head_dim")
-    if slot_mapping.numel() != n:
-        raise ValueError("slot_mapping must hold one slot per token")
+    if slot_mapping.numel() != n or value.shape[0] != n or value.shape[1] != hkv:
+        raise ValueError("key, value and slot_mapping must have the same number of tokens and heads")
     _i32(slot_mapping, "slot_mapping")
+    if k_cache.dtype != key.dtype or v_cache.dtype != key.dtype or value.dtype != key.dtype or \
+            k_cache.numel() != v_cache.numel():
+        raise ValueError("key, value and both caches must share one dtype, and the caches one size")
+    _same_device(key, value=value, k_cache=k_cache, v_cache=v_cache, slot_mapping=slot_mapping)
     num_slots = k_cache.numel() // D
     _check("pkv_store_kvcache",
            lib.pkv_store_kvcache(_ptr(key), ks, _ptr(value), vs, _ptr(k_cache), _ptr(v_cache), num_slots,
@@ -280,9 +322,17 @@ def attn_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, 
     _i32(cu_seqlens_q, "cu_seqlens_q")
     _i32(cu_seqlens_k, "cu_seqlens_k")
     nseq = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != nseq + 1:
+        raise ValueError(f"cu_seqlens_k must hold num_seqs + 1 = {nseq + 1} entries, got {cu_seqlens_k.numel()}")
+    if block_table is not None and (block_table.dim() != 2 or block_table.shape[0] < nseq):
+        raise ValueError(f"block_table must be [num_seqs >= {nseq}, max_blocks], got {tuple(block_table.shape)}")
+    if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16 or (block_table is not None and k.shape != v.shape):
+        raise ValueError("k and v must be bfloat16 (and, as caches, of the same shape)")
+    _same_device(q, k=k, v=v, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, block_table=block_table)
     scale = HEAD_DIM ** -0.5 if softmax_scale is None else softmax_scale
     if out is None:
         out = torch.empty((tq, hq, HEAD_DIM), dtype=torch.bfloat16, device=q.device)
+    _out(out, (tq, hq, HEAD_DIM), q, "out")
     _check("pkv_attn_prefill_varlen",
            lib.pkv_attn_prefill_varlen(_ptr(q), qs, _ptr(k), ks, _ptr(v), vs, _ptr(out), _ptr(cu_seqlens_q),
                                        _ptr(cu_seqlens_k), nseq, tq, int(max_seqlen_q), int(max_seqlen_k), hq, hkv,
@@ -316,13 +366,23 @@ def attn_decode_paged(q, k_cache, v_cache, cache_seqlens, block_table, softmax_s
     hkv, num_blocks = k_cache.shape[2], k_cache.shape[0]
     _i32(cache_seqlens, "cache_seqlens")
     _i32(block_table, "block_table")
+    if cache_seqlens.numel() != B or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"cache_seqlens [B] and block_table [B, max_blocks] must match q's B = {B}, got "
+                         f"{tuple(cache_seqlens.shape)} and {tuple(block_table.shape)}")
+    if k_cache.dtype != torch.bfloat16 or k_cache.shape != v_cache.shape:
+        raise ValueError("caches must be bfloat16 and of the same shape")
+    _same_device(q, k_cache=k_cache, v_cache=v_cache, cache_seqlens=cache_seqlens, block_table=block_table,
+                 workspace=workspace)
     mb = block_table.shape[1]
     scale = HEAD_DIM ** -0.5 if softmax_scale is None else softmax_scale
     need = decode_workspace_bytes(B, hq, hkv, mb)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
     if out is None:
         out = torch.empty((B, hq, HEAD_DIM), dtype=torch.bfloat16, device=q.device)
+    _out(out, (B, hq, HEAD_DIM), q, "out")
     _check("pkv_attn_decode_paged",
            lib.pkv_attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(cache_seqlens),
                                      _ptr(block_table), mb, B, hq, hkv, HEAD_DIM, BLOCK_SIZE, num_blocks,
@@ -343,10 +403,16 @@ def add_rms_norm(x, residual, weight, eps: float = 1.0e-6, y=None, residual_out=
     if residual is not None and (residual.shape != x.shape or residual.dtype != x.dtype or
                                  not residual.is_contiguous()):
         raise ValueError("residual must match x")
+    if weight.dtype != torch.bfloat16 or weight.numel() != hidden or not weight.is_contiguous():
+        raise ValueError(f"weight must be a contiguous bfloat16 tensor of {hidden} elements")
+    _same_device(x, residual=residual, weight=weight)
     if y is None:
         y = torch.empty_like(x)
     if residual is not None and residual_out is None:
         residual_out = torch.empty_like(x)
+    _out(y, x.shape, x, "y")
+    if residual is not None:
+        _out(residual_out, x.shape, x, "residual_out")
     _check("pkv_add_rms_norm",
            lib.pkv_add_rms_norm(_ptr(x), _ptr(residual), _ptr(weight), _ptr(y),
                                 _ptr(residual_out) if residual is not None else None, t, hidden, float(eps),
@@ -361,9 +427,13 @@ def silu_and_mul(x, out=None, stream=None):
     if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a bf16 [T, 2I] tensor with unit column stride")
     t, two_i = x.shape
+    if two_i % 2:
+        raise ValueError("x must hold gate and up halves of equal width")
     inter = two_i // 2
     if out is None:
         out = torch.empty((t, inter), dtype=torch.bfloat16, device=x.device)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (t, inter) or out.stride(1) != 1 or out.device != x.device:
+        raise ValueError(f"out must be a bfloat16 [{t}, {inter}] tensor with unit column stride on {x.device}")
     _check("pkv_silu_and_mul",
            lib.pkv_silu_and_mul(_ptr(x), x.stride(0), _ptr(out), out.stride(0), t, inter, _stream(stream)))
     return out
@@ -384,8 +454,11 @@ def sample_gumbel(logits, temperatures, seed: int = 0, offset: int = 0, noise=No
         raise ValueError("temperatures must be contiguous float32 [B]")
     if noise is not None and (noise.dtype != torch.float32 or noise.shape != logits.shape or noise.stride(1) != 1):
         raise ValueError("noise must be float32 [B, V]")
+    _same_device(logits, temperatures=temperatures, noise=noise)
     if out is None:
         out = torch.empty(b, dtype=torch.int64, device=logits.device)
+    if out.dtype != torch.int64 or out.numel() != b or not out.is_contiguous() or out.device != logits.device:
+        raise ValueError(f"out must be a contiguous int64 tensor of {b} elements on {logits.device}")
     _check("pkv_sample_gumbel",
            lib.pkv_sample_gumbel(_ptr(logits), logits.stride(0), dt, _ptr(temperatures), _ptr(noise),
                                  noise.stride(0) if noise is not None else 0, int(seed), int(offset), _ptr(out), b, v,

@@ -259,12 +259,12 @@ size_t pkv_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
     return pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq);
 }
 
-int pkv_attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, void* o,
-                          const int32_t* context_lens, const int32_t* block_table, int32_t max_blocks_per_seq,
-                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                          int32_t block_size, int64_t num_blocks, float softmax_scale, void* workspace,
-                          size_t workspace_bytes, void* stream) {
-    const char* fn = "pkv_attn_decode_paged";
+namespace {
+// Checks shared by the two decode entry points; on success fills `a` (workspace unset).
+int decode_args(const char* fn, const void* q, const void* k_cache, const void* v_cache, void* o,
+                const int32_t* context_lens, const int32_t* block_table, int32_t max_blocks_per_seq, int32_t num_seqs,
+                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                float softmax_scale, pkv::DecodeArgs& a) {
     int rc = check_heads(fn, num_q_heads, num_kv_heads, head_dim);
     if (rc) return rc;
     const int G = num_q_heads / num_kv_heads;
@@ -273,7 +273,7 @@ int pkv_attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
     PKV_REQUIRE(block_size == 256, PKV_ERR_UNSUPPORTED, "%s: block_size %d unsupported (only 256)", fn, block_size);
     PKV_REQUIRE(num_seqs >= 0, PKV_ERR_INVALID_ARG, "%s: num_seqs must be >= 0", fn);
     PKV_REQUIRE(max_blocks_per_seq > 0, PKV_ERR_INVALID_ARG, "%s: max_blocks_per_seq must be > 0", fn);
-    if (num_seqs == 0) return ok();
+    if (num_seqs == 0) return PKV_OK;
     PKV_REQUIRE(q && k_cache && v_cache && o && context_lens && block_table, PKV_ERR_INVALID_ARG,
                 "%s: a required pointer is NULL", fn);
     PKV_REQUIRE(k_cache != v_cache, PKV_ERR_INVALID_ARG, "%s: k_cache and v_cache must be distinct", fn);
@@ -281,12 +281,6 @@ int pkv_attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
     PKV_REQUIRE(softmax_scale > 0.f, PKV_ERR_INVALID_ARG, "%s: softmax_scale must be > 0", fn);
     PKV_REQUIRE(((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)o) % 16 == 0,
                 PKV_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
-    const size_t need = pkv_attn_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                        max_blocks_per_seq, block_size);
-    PKV_REQUIRE(workspace != nullptr && workspace_bytes >= need, PKV_ERR_WORKSPACE,
-                "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? workspace_bytes : (size_t)0);
-    PKV_REQUIRE((uintptr_t)workspace % 256 == 0, PKV_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
-    pkv::DecodeArgs a;
     a.q = q;
     a.k_cache = k_cache;
     a.v_cache = v_cache;
@@ -299,6 +293,27 @@ int pkv_attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
     a.hkv = num_kv_heads;
     a.num_blocks = num_blocks;
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.workspace = nullptr;
+    return PKV_OK;
+}
+}  // namespace
+
+int pkv_attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, void* o,
+                          const int32_t* context_lens, const int32_t* block_table, int32_t max_blocks_per_seq,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int64_t num_blocks, float softmax_scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    const char* fn = "pkv_attn_decode_paged";
+    pkv::DecodeArgs a;
+    int rc = decode_args(fn, q, k_cache, v_cache, o, context_lens, block_table, max_blocks_per_seq, num_seqs,
+                         num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, softmax_scale, a);
+    if (rc) return rc;
+    if (num_seqs == 0) return ok();
+    const size_t need = pkv_attn_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                        max_blocks_per_seq, block_size);
+    PKV_REQUIRE(workspace != nullptr && workspace_bytes >= need, PKV_ERR_WORKSPACE,
+                "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? workspace_bytes : (size_t)0);
+    PKV_REQUIRE((uintptr_t)workspace % 256 == 0, PKV_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
     a.workspace = workspace;
     return launched(pkv::launch_attn_decode(a, (hipStream_t)stream), fn);
 }

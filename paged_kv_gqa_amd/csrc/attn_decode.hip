@@ -224,9 +224,15 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
         float p[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) p[r] = exp2f(sv[r] - ref);
-        l_run = fmaf(l_run, alpha, (p[0] + p[1]) + (p[2] + p[3]));
-        // B operand of P V: keys 4*grp + r of column col -- the score layout itself
+        // B operand of P V: keys 4*grp + r of column col -- the score layout itself.
+        // The row sum adds the same bf16-rounded weights P V uses (dot2 with (1, 1)),
+        // so numerator and denominator agree.
         const bf16x4 pb = {(bf16)p[0], (bf16)p[1], (bf16)p[2], (bf16)p[3]};
+        const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+        const float psum = __builtin_amdgcn_fdot2_f32_bf16(
+            __builtin_shufflevector(pb, pb, 2, 3), ones,
+            __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), ones, 0.f, false), false);
+        l_run = fmaf(l_run, alpha, psum);
         // ---- O^T += V^T P on MFMA; V^T tiles by transposing LDS reads: lane j of the
         // 16-lane group grp addresses key 4*grp + j/4, dims 16d + 4*(j%4) and receives
         // dim 16d + j across those 4 keys.

@@ -38,15 +38,16 @@
 //     with 16-byte slots XOR-swizzled per row so the operand reads stay
 //     conflict-free.  The exact pass stages tiles through registers into padded
 //     rows (16-byte copies; rows past the last key clamped, V zeroed there).
-//   * Softmax in two passes.  The fast pass (one kernel) pre-scales Q by
-//     softmax_scale * log2(e) and takes exp2 of each score against a fixed
-//     reference of 0: no row max, no rescale, three VALU operations per score
-//     (exp2, add, half a bf16 pack) instead of five.  The reference cancels in
-//     O / l, so this is exact up to rounding while a row's weights stay far
-//     from overflow and underflow; a wave whose rows leave l in [2^-64, 2^64]
-//     (or whose O is not finite) writes a marker instead of its results.  The
-//     exact pass (a second, persistent kernel) recomputes only flagged work
-//     items, with Q as given, the scale in fp32, and an online running max that
+//   * Softmax in two passes.  The fast pass (one kernel) takes exp2 of each
+//     score times softmax_scale * log2(e) (fp32) against a fixed reference of
+//     0: no row max, no rescale, four VALU operations per score (multiply,
+//     exp2, add, half a bf16 pack) instead of five.  The reference cancels in
+//     O / l and floating point is scale-invariant away from its range limits,
+//     so the weights are the online softmax's up to fp32 rounding while a
+//     row's weights stay far from overflow and underflow; a wave whose rows
+//     leave l in [2^-64, 2^64] (or whose O is not finite) writes a marker
+//     instead of its results.  The exact pass (a second, persistent kernel)
+//     recomputes only flagged work items with an online running max that
 //     moves only when a row grows by more than 2^8.  A call with nothing
 //     flagged costs one short launch whose workgroups read one word and exit;
 //     batches under 2e10 FLOP run the exact pass alone in one launch.
@@ -81,6 +82,7 @@ constexpr int kTileKeys = NW == 8 ? 128 : 64;
 // the exact pass: a signalling-NaN pattern, which no arithmetic result converted
 // to bf16 can have (those NaNs are quiet).
 constexpr uint16_t kFixupMarker = 0x7F81;
+constexpr bf16x2 kOnes2 = {(bf16)1.0f, (bf16)1.0f};
 }  // namespace
 
 // Highest call number (see launch_attn_prefill) whose fast pass flagged a work
@@ -155,23 +157,17 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
     const int wave_tiles = (wave_keys + kKT - 1) / kKT;
 
     // ---- Q^T as the B operand: lane owns query row l%32, dims 8*(l/32) + 16*st .. +7.
-    // For the fast pass Q is multiplied by softmax_scale * log2(e) here (fp32,
-    // rounded back to bf16), so its products are scores in base-2 exponent units.
+    // Q stays as given (bf16): its products with K are exact in the fp32
+    // accumulator, and the scale is applied to each score in fp32.  (Rounding
+    // Q * scale back to bf16 instead would move every score by up to 2^-9 of the
+    // sum of |q_i k_i| -- an error that grows with the score.)
     const int qi = wp0 + (lane & 31);
     const int q_row = cq0 + min(qi, Lq - 1);
     const uint16_t* qp = (const uint16_t*)a.q + (int64_t)min(q_row, a.total_q - 1) * a.q_row_stride +
                          (int64_t)head * kHeadDim + 8 * (lane >> 5);
     bf16x8 qreg[8];
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-        u32x4 w = ldg128(qp + 16 * st);
-        if (!kExact) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                w[e] = pack_bf16x2(bf16lo(w[e]) * a.scale_log2, bf16hi(w[e]) * a.scale_log2);
-        }
-        qreg[st] = __builtin_bit_cast(bf16x8, w);
-    }
+    for (int st = 0; st < 8; ++st) qreg[st] = __builtin_bit_cast(bf16x8, ldg128(qp + 16 * st));
     const int qpos = off + qi;                          // absolute position of this lane's query
 
     // ---- tile loaders.  Row strides are at most 2^24 elements (checked by the
@@ -357,17 +353,17 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
     // registers one iteration earlier) is stored into the other buffer; tile t+2 is
     // loaded after the barrier.  Fast pass: right after the barrier, tile t+1 is
     // copied straight into the other buffer while tile t is computed.
-    //   Fast pass (kExact false): Q pre-scaled, the weights are exp2(score) against
-    //   a fixed reference of 0 -- no row max, no rescale, one VALU op less per score.
-    //   Softmax does not depend on the reference and floating point is
+    //   Fast pass (kExact false): the weights are exp2(score * scale * log2 e)
+    //   against a fixed reference of 0 -- no row max, no rescale, one VALU op less
+    //   per score.  Softmax does not depend on the reference and floating point is
     //   scale-invariant away from overflow and underflow, so this is the same
     //   computation while a row's sum stays inside [2^-64, 2^64] and its O finite
-    //   (scores within about +-64 in base-2 units, where rounding the scaled Q to
-    //   bf16 moves a weight by less than bf16 rounding of P does); checked afterwards.
-    //   Exact pass (kExact true): Q as given, scale applied in fp32, and the online
-    //   softmax with a lazy reference max that moves only when a row grows by more
-    //   than 2^8, so the O rescale is skipped on most tiles.  Exact for any input:
-    //   O and l always share the reference.
+    //   (scores within about +-64 in base-2 units); checked afterwards.  Weights
+    //   below 2^-126 then sit more than 2^-62 / keys under the row's largest and
+    //   do not matter.
+    //   Exact pass (kExact true): the online softmax with a lazy reference max that
+    //   moves only when a row grows by more than 2^8, so the O rescale is skipped
+    //   on most tiles.  Exact for any input: O and l always share the reference.
     {
         bool ok_cur = false;   // fast pass: whether tile t's block id is usable, found when its copies were issued
         int32_t blk_next = 0;  // fast pass: block id of tile t+1
@@ -445,8 +441,8 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
             }
             if (v_later) issue_half(t + 1, (t + 1) & 1, blk1, true);
             if (live_t) {
-                // s[kh][r] = score of key j0 + 32kh + 8(r/4) + 4*h32 + r%4 for query qi
-                // (base-2 units in the fast pass, raw in the exact pass).
+                // s[kh][r] = raw score (q . k, unscaled) of key j0 + 32kh + 8(r/4) + 4*h32 + r%4
+                // for query qi.
                 const bool need_mask = !ok || (j0 + kKT - 1 > off + wp0) || (j0 + kKT > Lk);
                 if (need_mask) {
                     // key j0 + 4*h32 + c (c a compile-time offset) is visible iff c <= lim
@@ -487,20 +483,28 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
                     }
                     moff = m_run == -INFINITY ? 0.f : -m_run * a.scale_log2;
                 }
-                float psum = 0.f;
+                // The weights enter P V rounded to bf16; the row sum adds up those same
+                // rounded weights (bf16 dot2 with (1, 1), fp32 accumulate), so numerator
+                // and denominator agree: a row dominated by one key returns that key's
+                // value, not the value scaled by that weight's rounding error.
+                float psum0 = 0.f, psum1 = 0.f;
                 uint32_t pk[kKH][8];
 #pragma unroll
                 for (int kh = 0; kh < kKH; ++kh)
 #pragma unroll
                     for (int r = 0; r < 16; r += 2) {
-                        const float x0 = kExact ? fmaf(s[kh][r], a.scale_log2, moff) : s[kh][r];
-                        const float x1 = kExact ? fmaf(s[kh][r + 1], a.scale_log2, moff) : s[kh][r + 1];
+                        const float x0 = kExact ? fmaf(s[kh][r], a.scale_log2, moff) : s[kh][r] * a.scale_log2;
+                        const float x1 = kExact ? fmaf(s[kh][r + 1], a.scale_log2, moff) : s[kh][r + 1] * a.scale_log2;
                         const float e0 = __builtin_amdgcn_exp2f(x0);
                         const float e1 = __builtin_amdgcn_exp2f(x1);
-                        psum += e0 + e1;
-                        pk[kh][r >> 1] = pack_bf16x2(e0, e1);
+                        const uint32_t pw = pack_bf16x2(e0, e1);
+                        pk[kh][r >> 1] = pw;
+                        if (r & 2)
+                            psum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw), kOnes2, psum1, false);
+                        else
+                            psum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw), kOnes2, psum0, false);
                     }
-                l_part += psum;
+                l_part += psum0 + psum1;
 
                 // ---- O^T += V^T P^T: per 16-key step (kh, v) the B operand is registers 8v..8v+7 of s[kh].
                 // The A operand (V^T: row d = lane%32, 8 keys) comes from row-major V with two

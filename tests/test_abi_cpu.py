@@ -223,3 +223,30 @@ def test_sublayer_ops_validation(lib):
     assert h(FAKE, 151936, 0, T, R, 151935, 1, 0, TOK, 4, 151936, None) == -1                # noise stride
     assert h(FAKE, 151936, 0, None, None, 0, 1, 0, TOK, 4, 151936, None) == -1               # temperatures
     assert h(None, 151936, 0, None, None, 0, 1, 0, None, 0, 151936, None) == 0               # no rows
+
+
+def test_binding_refuses_mismatched_metadata_before_any_call(lib):
+    """The Python binding checks metadata counts and where tensors live before it passes
+    pointers on: a short cu_seqlens_k, a block table with fewer rows than sequences, a
+    context-length vector of the wrong size, or host tensors, raise ValueError."""
+    import torch
+    bf = torch.bfloat16
+    q = torch.zeros((10, 4, 128), dtype=bf)
+    k = torch.zeros((10, 2, 128), dtype=bf)
+    cu2 = torch.tensor([0, 4, 10], dtype=torch.int32)
+    with pytest.raises(ValueError, match="cu_seqlens_k"):
+        pkv.attn_prefill_varlen(q, k, k, cu2, torch.tensor([0, 10], dtype=torch.int32), 6, 6)
+    kc = torch.zeros((3, 256, 2, 128), dtype=bf)
+    with pytest.raises(ValueError, match="block_table"):
+        pkv.attn_prefill_varlen(q, kc, kc, cu2, cu2, 6, 6, block_table=torch.zeros((1, 3), dtype=torch.int32))
+    with pytest.raises(ValueError, match="GPU"):
+        pkv.attn_prefill_varlen(q, k, k, cu2, cu2, 6, 6)
+    qd = torch.zeros((3, 4, 128), dtype=bf)
+    with pytest.raises(ValueError, match="cache_seqlens"):
+        pkv.attn_decode_paged(qd, kc, kc, torch.zeros(2, dtype=torch.int32), torch.zeros((3, 2), dtype=torch.int32))
+    with pytest.raises(ValueError, match="cache_seqlens"):
+        pkv.attn_decode_paged(qd, kc, kc, torch.zeros(3, dtype=torch.int32), torch.zeros((2, 2), dtype=torch.int32))
+    with pytest.raises(ValueError, match="GPU"):
+        pkv.attn_decode_paged(qd, kc, kc, torch.zeros(3, dtype=torch.int32), torch.zeros((3, 2), dtype=torch.int32))
+    with pytest.raises(ValueError, match="same number"):
+        pkv.store_kvcache(k, k[:5], kc, kc, torch.zeros(10, dtype=torch.int32))
