@@ -241,6 +241,30 @@ PKV_API int pkv_attn_decode_paged(const void* q, const void* k_cache, const void
                           size_t workspace_bytes, void* stream);
 
 /*
+ * pkv_attn_decode_paged_noalloc -- pkv_attn_decode_paged without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).  The
+ * same kernels run; the split-K partials live in a fixed device array inside
+ * the library (one per GPU, 96 MiB, kept until the process ends).  Arguments,
+ * layouts and results are those of pkv_attn_decode_paged, byte for byte.
+ *
+ *   Sizes: a call needing more than 96 MiB of workspace (see
+ *   pkv_attn_decode_workspace_bytes; the Qwen3-8B batch of 256 sequences with
+ *   128-block tables needs 65 MiB) returns PKV_ERR_WORKSPACE and launches
+ *   nothing.  Nothing is allocated or freed; the first call on a device looks
+ *   up the array's device address once.
+ *   Concurrency: every call on one GPU uses the same array, so calls whose
+ *   execution overlaps on one GPU (different streams, or different host
+ *   threads) race and must be serialised by the caller; calls in order on one
+ *   stream are safe.
+ */
+PKV_API int pkv_attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o,
+                                  const int32_t* context_lens, const int32_t* block_table,
+                                  int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                  float softmax_scale, void* stream);
+
+/*
  * pkv_add_rms_norm -- residual add folded into RMSNorm, [Ops] s2 (RMSNorm
  * and its residual entry point); [TwoWays] s3.6 (one pass: read x and the
  * residual, write y and the new residual).  Per row of `hidden` elements:

@@ -43,7 +43,8 @@ EXPORTED = ("pkv_last_error", "pkv_version", "pkv_rope_cache_build", "pkv_qk_nor
             "pkv_qk_norm_rope_store", "pkv_store_kvcache", "pkv_attn_prefill_varlen",
             "pkv_attn_decode_workspace_bytes", "pkv_attn_decode_paged", "pkv_decode_step_workspace_bytes",
             "pkv_decode_step", "pkv_decode_graph_create", "pkv_decode_graph_bucket", "pkv_decode_graph_launch",
-            "pkv_decode_graph_destroy", "pkv_add_rms_norm", "pkv_silu_and_mul", "pkv_sample_gumbel")
+            "pkv_decode_graph_destroy", "pkv_add_rms_norm", "pkv_silu_and_mul", "pkv_sample_gumbel",
+            "pkv_attn_decode_paged_noalloc")
 
 #: the batch ladder the decode graphs are captured for
 GRAPH_BUCKETS = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
@@ -100,6 +101,8 @@ def load_library(path: str = LIB_PATH):
     lib.pkv_attn_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
     lib.pkv_attn_decode_workspace_bytes.restype = SZ
     lib.pkv_attn_decode_paged.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I64, F32, P, SZ, P]
+    lib.pkv_attn_decode_paged_noalloc.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I64, F32, P]
+    lib.pkv_attn_decode_paged_noalloc.restype = ctypes.c_int
     lib.pkv_attn_decode_paged.restype = ctypes.c_int
     lib.pkv_add_rms_norm.argtypes = [P, P, P, P, P, I32, I32, F32, P]
     lib.pkv_add_rms_norm.restype = ctypes.c_int

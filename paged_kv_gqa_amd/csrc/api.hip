@@ -318,6 +318,31 @@ int pkv_attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
     return launched(pkv::launch_attn_decode(a, (hipStream_t)stream), fn);
 }
 
+int pkv_attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o,
+                                  const int32_t* context_lens, const int32_t* block_table,
+                                  int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                  float softmax_scale, void* stream) {
+    const char* fn = "pkv_attn_decode_paged_noalloc";
+    pkv::DecodeArgs a;
+    int rc = decode_args(fn, q, k_cache, v_cache, o, context_lens, block_table, max_blocks_per_seq, num_seqs,
+                         num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, softmax_scale, a);
+    if (rc) return rc;
+    if (num_seqs == 0) return ok();
+    const size_t need = pkv_attn_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                        max_blocks_per_seq, block_size);
+    PKV_REQUIRE(need <= pkv::kDecodeScratchBytes, PKV_ERR_WORKSPACE,
+                "%s: this batch needs %zu bytes of split-K workspace, more than the %zu of the library's fixed "
+                "device array; call pkv_attn_decode_paged with a workspace instead",
+                fn, need, pkv::kDecodeScratchBytes);
+    void* ws = nullptr;
+    hipError_t e = pkv::decode_scratch(&ws);
+    if (e != hipSuccess)
+        return fail(PKV_ERR_LAUNCH, "%s: device address of the fixed workspace: %s", fn, hipGetErrorString(e));
+    a.workspace = ws;
+    return launched(pkv::launch_attn_decode(a, (hipStream_t)stream), fn);
+}
+
 int pkv_add_rms_norm(const void* x, const void* residual, const void* weight, void* y, void* residual_out,
                      int32_t n_tokens, int32_t hidden, float eps, void* stream) {
     const char* fn = "pkv_add_rms_norm";

@@ -38,6 +38,8 @@
 //   * Each wave writes its split's (m, l, O) to a caller-owned fp32 workspace
 //     and a second kernel merges the splits of each (b, h) in split order
 //     (deterministic).
+#include <mutex>
+
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -373,6 +375,41 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(const int32_t* __re
     }
     const float r = L > 0.f ? acc / L : 0.f;
     o[bh * kHeadDim + d] = __builtin_bit_cast(uint16_t, (bf16)r);
+}
+
+// ---- split-K workspace in a fixed device array, for pkv_attn_decode_paged_noalloc.
+// Callers that cannot allocate (code under graph capture, tight serving loops)
+// get the partials (m, l, O) and the dispatch order here instead of in a
+// workspace they pass.  One copy per GPU, held until the process ends; every
+// call on a GPU uses the same bytes, so calls that overlap on one GPU race.
+// Nothing in it needs clearing between calls: the order kernel writes the whole
+// dispatch list, and the merge reads only the splits the split kernel wrote in
+// the same call.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Device address of `scratch` on the current device, looked up once per device
+// (the host-side name of the array is not a device address).
+hipError_t decode_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr || (uintptr_t)p % 256 != 0) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t stream) {

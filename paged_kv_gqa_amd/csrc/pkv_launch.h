@@ -86,5 +86,9 @@ struct DecodeArgs {
 int decode_split_blocks(int32_t num_seqs, int32_t hkv, int32_t max_blocks);
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t max_blocks);
 hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t stream);
+// Size of the fixed device array pkv_attn_decode_paged_noalloc uses as its workspace.
+constexpr size_t kDecodeScratchBytes = size_t(96) << 20;
+// Its device address on the current device (looked up once per device).
+hipError_t decode_scratch(void** ptr);
 
 }  // namespace pkv
