@@ -268,6 +268,7 @@ def main():
 
     ladder = decode_graph_ladder(pkv, torch, s8, table, qkv_d, kc_d, vc_d, pos_d, slot_d, cl_d, bt_d, gq_d, gk_d,
                                  args, log)
+    ladder_short = decode_graph_short(pkv, torch, dev, to_dev, table, args, log)
 
     cpu = cpu_pre = cpu_st = cpu_one = None
     if not args.no_cpu_baseline:
@@ -316,6 +317,7 @@ def main():
         "qk_norm_rope_small": norm_small,
         "qwen3_0_6b": small,
         "decode_graph": ladder,
+        "decode_graph_short": ladder_short,
         "cpu_baseline_prefill": cpu_pre,
         "cpu_baseline_stages": cpu_st,
         "cpu_baseline_one_thread": cpu_one,
@@ -518,6 +520,79 @@ def decode_graph_ladder(pkv, torch, s8, table, qkv_d, kc_d, vc_d, pos_d, slot_d,
             out["back_to_back"][mode][str(b)] = round((time.perf_counter() - t0) * 1e6 / reps, 2)
     st.close()
     log(f"decode graph ladder (us/step): {json.dumps(out)}")
+    return out
+
+
+def decode_graph_short(pkv, torch, dev, to_dev, table, args, log):
+    """Decode step on short contexts (64 sequences, contexts U[256, 1024], 32/8 heads), where
+    launch overhead rather than K/V bytes sets the time: eager vs HIP-graph replay per bucket
+    B = 1 ... 64 (latency: launch then synchronise; back_to_back: consecutive steps), and at
+    batches between buckets (3, 12, 48) the replay with the library's padding launch vs the
+    caller keeping the padded rows itself (PKV_DECODE_CALLER_PADS)."""
+    import workloads as wl
+    w = wl.short_decode_8b(args.seed)
+    s8 = w.shape
+    kc = torch.empty((w.num_blocks, 256, s8.num_kv_heads, 128), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    wl.fill_normal_bf16_(kc, 6, args.seed, 10)
+    wl.fill_normal_bf16_(vc, 6, args.seed, 11)
+    qkv = to_dev(w.qkv())
+    gq, gk = (to_dev(g) for g in w.gammas())
+    pos, slot = to_dev(w.positions), to_dev(w.slot_mapping)
+    cl, bt = to_dev(w.context_lens), to_dev(w.block_tables)
+    reps = max(args.steps, 50)
+
+    def timing(fn, b):
+        for _ in range(5):
+            fn(b)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn(b)
+            torch.cuda.synchronize()
+        lat = (time.perf_counter() - t0) * 1e6 / reps
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn(b)
+        torch.cuda.synchronize()
+        return round(lat, 2), round((time.perf_counter() - t0) * 1e6 / reps, 2)
+
+    out = {"workload": f"{w.batch} sequences of the 8B shapes, contexts U[256, 1024] (mean "
+                       f"{float(w.context_lens.mean()):.0f}); one step = qk_norm_rope_store + paged decode",
+           "unit": "us/step", "latency": {"eager": {}, "graph": {}}, "back_to_back": {"eager": {}, "graph": {}},
+           "between_buckets": {}}
+    st = pkv.DecodeStep(qkv, kc, vc, pos, slot, cl, bt, gq, gk, table, s8.num_q_heads, s8.num_kv_heads, eps=s8.eps)
+    st.capture()
+    for b in st.buckets:
+        for mode, fn in (("eager", st.run), ("graph", st.replay)):
+            lat, btb = timing(fn, b)
+            out["latency"][mode][str(b)] = lat
+            out["back_to_back"][mode][str(b)] = btb
+    st.close()
+    # between buckets: the library pads rows [b, bucket) with one kernel per replay, or the
+    # caller keeps them padded (slot -1, context 0) and the replay is the graph alone
+    slot_p, cl_p = slot.clone(), cl.clone()
+    stc = pkv.DecodeStep(qkv, kc, vc, pos, slot_p, cl_p, bt, gq, gk, table, s8.num_q_heads, s8.num_kv_heads,
+                         eps=s8.eps, caller_pads=True)
+    stc.capture()
+    stl = pkv.DecodeStep(qkv, kc, vc, pos, slot.clone(), cl.clone(), bt, gq, gk, table, s8.num_q_heads,
+                         s8.num_kv_heads, eps=s8.eps)
+    stl.capture()
+    for b in (3, 12, 48):
+        n = stc.bucket(b)
+        slot_p.copy_(slot)
+        cl_p.copy_(cl)
+        slot_p[b:n] = -1
+        cl_p[b:n] = 0
+        torch.cuda.synchronize()
+        lat_l, btb_l = timing(stl.replay, b)
+        lat_c, btb_c = timing(stc.replay, b)
+        out["between_buckets"][str(b)] = {"bucket": n, "library_pads": {"latency": lat_l, "back_to_back": btb_l},
+                                          "caller_pads": {"latency": lat_c, "back_to_back": btb_c}}
+    stc.close()
+    stl.close()
+    log(f"decode graph, short contexts (us/step): {json.dumps(out)}")
+    del kc, vc
     return out
 
 

@@ -314,8 +314,12 @@ PKV_API int pkv_silu_and_mul(const void* x, int64_t x_row_stride, void* out, int
  *                      (column / 4, row, offset low, offset high), word column % 4;
  *                      the top 24 bits k give u = (k + 1) / 2^24 and E = -ln(u).
  *                      Otherwise fp32 [num_rows][noise_row_stride] holding E.
- *   tokens             int64 [num_rows], written.
- * Rows whose scores are all NaN return token 0.
+ *   tokens             int64 [num_rows], 8-byte aligned, written.  During the
+ *                      call it also serves as each row's reduction slot (the
+ *                      row's workgroups combine their winners there with 64-bit
+ *                      atomics), so it must not overlap the other arguments.
+ * Rows whose scores are all NaN return token 0.  Three launches on `stream`:
+ * clear the slots, sample, turn each slot's key into the token index.
  */
 PKV_API int pkv_sample_gumbel(const void* logits, int64_t logits_row_stride, int32_t logits_dtype,
                               const float* temperatures, const float* noise, int64_t noise_row_stride, uint64_t seed,
@@ -336,6 +340,12 @@ PKV_API int pkv_sample_gumbel(const void* logits, int64_t logits_row_stride, int
  * while a graph built from the descriptor exists (a graph bakes them in): a
  * caller writes each step's inputs into them, then launches.
  */
+/* pkv_decode_step_desc.flags: the caller keeps rows [batch, bucket) of
+ * slot_mapping and context_lens at -1 and 0 itself (as the pages' runner fills
+ * its static buffers before a replay), so pkv_decode_graph_launch enqueues the
+ * captured graph alone, without its one-kernel padding step. */
+#define PKV_DECODE_CALLER_PADS 1
+
 typedef struct {
     const void* qkv;             /* bf16 [max_batch][qkv_row_stride]: q | k | v column blocks (a1 views) */
     int64_t qkv_row_stride;      /* elements, >= (Hq + 2 Hkv) * head_dim, multiple of 8 */
@@ -345,8 +355,10 @@ typedef struct {
     void* v_cache;
     int64_t num_blocks;
     const int64_t* positions;    /* int64 [max_batch] */
-    int32_t* slot_mapping;       /* int32 [max_batch]; a graph launch writes -1 into padded rows */
-    int32_t* context_lens;       /* int32 [max_batch]; a graph launch writes 0 into padded rows */
+    int32_t* slot_mapping;       /* int32 [max_batch]; a graph launch writes -1 into padded rows
+                                    (unless flags has PKV_DECODE_CALLER_PADS) */
+    int32_t* context_lens;       /* int32 [max_batch]; a graph launch writes 0 into padded rows
+                                    (unless flags has PKV_DECODE_CALLER_PADS) */
     const int32_t* block_table;  /* int32 [max_batch][max_blocks_per_seq] */
     int32_t max_blocks_per_seq;
     int32_t max_batch;
@@ -360,7 +372,7 @@ typedef struct {
     int32_t head_dim;            /* 128 */
     int32_t block_size;          /* 256 */
     float softmax_scale;
-    int32_t reserved;            /* set to 0 */
+    int32_t flags;               /* 0 or PKV_DECODE_CALLER_PADS */
     void* workspace;             /* >= pkv_decode_step_workspace_bytes(max_batch, ...), 256-byte aligned */
     size_t workspace_bytes;
 } pkv_decode_step_desc;

@@ -46,6 +46,9 @@ EXPORTED = ("pkv_last_error", "pkv_version", "pkv_rope_cache_build", "pkv_qk_nor
             "pkv_decode_graph_destroy", "pkv_add_rms_norm", "pkv_silu_and_mul", "pkv_sample_gumbel",
             "pkv_attn_decode_paged_noalloc")
 
+#: pkv_decode_step_desc.flags bit: the caller pads rows [batch, bucket) itself before a graph launch
+PKV_DECODE_CALLER_PADS = 1
+
 #: the batch ladder the decode graphs are captured for
 GRAPH_BUCKETS = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
 
@@ -60,7 +63,7 @@ class DecodeStepDesc(ctypes.Structure):
                 ("q_norm_weight", ctypes.c_void_p), ("k_norm_weight", ctypes.c_void_p),
                 ("cos_sin_cache", ctypes.c_void_p), ("max_position", ctypes.c_int32), ("eps", ctypes.c_float),
                 ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("block_size", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("flags", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 _lib = None
@@ -478,12 +481,14 @@ class DecodeStep:
     each step.  ``run(batch)`` launches the kernels eagerly; ``capture()``
     records one HIP graph per bucket and ``replay(batch)`` pads rows
     [batch, bucket) (slot -1, context 0) and launches the bucket's graph.
+    With ``caller_pads=True`` the caller keeps those rows padded itself and a
+    replay launches the graph alone.
     Outputs: ``q_out`` (q') and ``o`` [max_batch, Hq, 128].
     """
 
     def __init__(self, qkv, k_cache, v_cache, positions, slot_mapping, context_lens, block_table, q_norm_weight,
                  k_norm_weight, cos_sin_cache, num_q_heads: int, num_kv_heads: int, eps: float = 1.0e-6,
-                 softmax_scale: Optional[float] = None):
+                 softmax_scale: Optional[float] = None, caller_pads: bool = False):
         import torch
         lib = load_library()
         mb = qkv.shape[0]
@@ -519,7 +524,8 @@ class DecodeStep:
             k_norm_weight=_ptr(k_norm_weight), cos_sin_cache=_ptr(cos_sin_cache),
             max_position=cos_sin_cache.shape[0], eps=float(eps), num_q_heads=num_q_heads,
             num_kv_heads=num_kv_heads, head_dim=HEAD_DIM, block_size=BLOCK_SIZE,
-            softmax_scale=HEAD_DIM ** -0.5 if softmax_scale is None else float(softmax_scale), reserved=0,
+            softmax_scale=HEAD_DIM ** -0.5 if softmax_scale is None else float(softmax_scale),
+            flags=PKV_DECODE_CALLER_PADS if caller_pads else 0,
             workspace=_ptr(self.workspace), workspace_bytes=need)
         self._graph = None
         self.buckets = ()

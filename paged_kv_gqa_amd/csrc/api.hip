@@ -404,6 +404,7 @@ int pkv_sample_gumbel(const void* logits, int64_t logits_row_stride, int32_t log
     PKV_REQUIRE(logits && temperatures && tokens, PKV_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
     PKV_REQUIRE(((uintptr_t)logits | (uintptr_t)noise) % 16 == 0, PKV_ERR_INVALID_ARG,
                 "%s: logits and noise must be 16-byte aligned", fn);
+    PKV_REQUIRE((uintptr_t)tokens % 8 == 0, PKV_ERR_INVALID_ARG, "%s: tokens must be 8-byte aligned", fn);
     return launched(pkv::launch_sample_gumbel(logits, logits_row_stride, logits_dtype == PKV_DTYPE_F32, temperatures,
                                               noise, noise_row_stride, seed, offset, tokens, num_rows, vocab,
                                               (hipStream_t)stream),

@@ -325,21 +325,18 @@ __global__ void __launch_bounds__(1024) decode_order_kernel(const int32_t* __res
     }
 }
 
-// One workgroup of 128 threads per (b, h): merge the splits in order.  The
-// splits are taken 128 at a time: their (m, l) pairs are loaded by the whole
-// workgroup at once and their weights exp2(m_s - M) staged in LDS, then each
-// thread (one output dim) sums its column of partial outputs with the loads
-// unrolled, so a long context (many splits) costs a few memory latencies, not
-// one per split.  The sums run over s in increasing order, as a serial merge.
-__global__ void __launch_bounds__(128) decode_combine_kernel(const int32_t* __restrict__ context_lens,
-                                                             int32_t max_blocks, int32_t hq, int32_t split_blocks,
-                                                             int32_t max_splits, const float* __restrict__ part_o,
-                                                             const float* __restrict__ part_ml,
-                                                             uint16_t* __restrict__ o) {
-    __shared__ float s_w[128];
-    __shared__ float s_l[128];
-    __shared__ float s_red[2];
-    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+// Merge of the splits of each (b, h), in split order: one wave per (b, h), four
+// per workgroup, each lane owning two output dims.  The (m, l) pairs are read
+// with uniform addresses (every lane the same split), the partial outputs as
+// 512 contiguous bytes per split, four splits' loads in flight at a time.
+constexpr int kCombineWaves = 4;
+__global__ void __launch_bounds__(64 * kCombineWaves) decode_combine_kernel(
+    const int32_t* __restrict__ context_lens, int32_t max_blocks, int32_t hq, int32_t split_blocks,
+    int32_t max_splits, const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    uint16_t* __restrict__ o) {
+    const int lane = threadIdx.x & 63;
+    const int h = blockIdx.x * kCombineWaves + (threadIdx.x >> 6), b = blockIdx.y;
+    if (h >= hq) return;
     int ctx = context_lens[b];
     const int cap = max_blocks * kBlockSize;
     ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
@@ -347,34 +344,42 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(const int32_t* __re
     const int ns = (nblk + split_blocks - 1) / split_blocks;
     const int64_t bh = (int64_t)b * hq + h;
     const float* ml = part_ml + bh * max_splits * 2;
-    const float* po = part_o + bh * max_splits * kHeadDim + d;
+    const float* po = part_o + bh * max_splits * kHeadDim + 2 * lane;
 
     float M = -INFINITY;
-    for (int s = d; s < ns; s += 128) M = fmaxf(M, ml[2 * s]);
+    for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
     M = wave_max(M);
-    if ((d & 63) == 0) s_red[d >> 6] = M;
-    __syncthreads();
-    M = fmaxf(s_red[0], s_red[1]);
     const float ref = M == -INFINITY ? 0.f : M;
 
-    float L = 0.f, acc = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += 128) {
-        const int n = ns - s0 < 128 ? ns - s0 : 128;
-        if (d < n) {
-            s_w[d] = exp2f(ml[2 * (s0 + d)] - ref);
-            s_l[d] = ml[2 * (s0 + d) + 1];
+    float L = 0.f;
+    float acc0 = 0.f, acc1 = 0.f;
+    int s = 0;
+    for (; s + 4 <= ns; s += 4) {
+        float2 p[4];
+        float m[4], l[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[i] = *reinterpret_cast<const float2*>(po + (int64_t)(s + i) * kHeadDim);
+            m[i] = ml[2 * (s + i)];
+            l[i] = ml[2 * (s + i) + 1];
         }
-        __syncthreads();
-#pragma unroll 8
-        for (int i = 0; i < n; ++i) {
-            const float w = s_w[i];
-            L = fmaf(s_l[i], w, L);
-            acc = fmaf(po[(int64_t)(s0 + i) * kHeadDim], w, acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float w = exp2f(m[i] - ref);
+            L = fmaf(l[i], w, L);
+            acc0 = fmaf(p[i].x, w, acc0);
+            acc1 = fmaf(p[i].y, w, acc1);
         }
-        __syncthreads();
     }
-    const float r = L > 0.f ? acc / L : 0.f;
-    o[bh * kHeadDim + d] = __builtin_bit_cast(uint16_t, (bf16)r);
+    for (; s < ns; ++s) {
+        const float2 p = *reinterpret_cast<const float2*>(po + (int64_t)s * kHeadDim);
+        const float w = exp2f(ml[2 * s] - ref);
+        L = fmaf(ml[2 * s + 1], w, L);
+        acc0 = fmaf(p.x, w, acc0);
+        acc1 = fmaf(p.y, w, acc1);
+    }
+    const float r0 = L > 0.f ? acc0 / L : 0.f, r1 = L > 0.f ? acc1 / L : 0.f;
+    *reinterpret_cast<uint32_t*>(o + bh * kHeadDim + 2 * lane) = pack_bf16x2(r0, r1);
 }
 
 // ---- split-K workspace in a fixed device array, for pkv_attn_decode_paged_noalloc.
@@ -440,7 +445,8 @@ hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t stream) {
 #undef PKV_DECODE_CASE
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(a.hq, a.num_seqs), dim3(kHeadDim), 0, stream, a.context_lens,
+    hipLaunchKernelGGL(decode_combine_kernel, dim3((a.hq + kCombineWaves - 1) / kCombineWaves, a.num_seqs),
+                       dim3(64 * kCombineWaves), 0, stream, a.context_lens,
                        a.max_blocks, a.hq, sb, ms, w.part_o, w.part_ml, (uint16_t*)a.o);
     return hipGetLastError();
 }

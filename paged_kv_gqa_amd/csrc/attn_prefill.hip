@@ -406,6 +406,11 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
             bool ok = ok_cur;
             if (!kDma) (void)tile_row0(t, ok);
             f32x16 s[kKH];
+            // Fast pass: the QK^T phase (MFMA only) runs at raised wave priority and the
+            // softmax + P V phase (VALU-heavy) at the normal one, so of the two waves on a
+            // SIMD the one still issuing QK^T MFMAs goes first while the other works
+            // through its exponentials (measured +1.5 to 2.5% on the 8B prefix batch).
+            if (kDma) __builtin_amdgcn_s_setprio(3);
             if (live_t) {
                 // ---- S^T = K Q^T for the tile's 32-key blocks
                 // The key blocks are independent accumulation chains; interleaving them
@@ -439,6 +444,7 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
                     __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
                 }
             }
+            if (kDma) __builtin_amdgcn_s_setprio(0);
             if (v_later) issue_half(t + 1, (t + 1) & 1, blk1, true);
             if (live_t) {
                 // s[kh][r] = raw score (q . k, unscaled) of key j0 + 32kh + 8(r/4) + 4*h32 + r%4

@@ -12,7 +12,9 @@
 // One step = pkv_qk_norm_rope_store over the step's qkv rows (q', and k' / v
 // into their cache slots) followed by pkv_attn_decode_paged.  The graph for
 // bucket n is exactly the eager step at batch n, captured once; a replay for
-// a batch b < n first marks rows [b, n) as padding with one small kernel.
+// a batch b < n first marks rows [b, n) as padding with one small kernel,
+// unless the caller keeps those rows padded itself (PKV_DECODE_CALLER_PADS),
+// as the pages' runner does when it fills its static buffers.
 #include <new>
 
 #include "pkv.h"
@@ -59,6 +61,8 @@ int check_desc(const pkv_decode_step_desc* d) {
     if (d->qkv_row_stride < width)
         return set_error(PKV_ERR_INVALID_ARG, "decode step: qkv_row_stride %lld < (Hq + 2 Hkv) * head_dim = %lld",
                      (long long)d->qkv_row_stride, (long long)width);
+    if (d->flags & ~PKV_DECODE_CALLER_PADS)
+        return set_error(PKV_ERR_INVALID_ARG, "decode step: unknown flags 0x%x", (unsigned)d->flags);
     if (d->num_blocks <= 0 || d->block_size != 256)
         return set_error(PKV_ERR_INVALID_ARG, "decode step: needs num_blocks > 0 and block_size 256");
     const size_t need = pkv_decode_step_workspace_bytes(d->max_batch, d->num_q_heads, d->num_kv_heads,
@@ -184,7 +188,7 @@ int pkv_decode_graph_launch(pkv_decode_graph g, int32_t batch, void* stream) {
                      g->buckets[g->num_buckets - 1]);
     const int32_t n = g->buckets[i];
     hipStream_t s = (hipStream_t)stream;
-    if (n > batch) {
+    if (n > batch && !(g->desc.flags & PKV_DECODE_CALLER_PADS)) {
         const unsigned blocks = (unsigned)((n - batch + 255) / 256);
         hipLaunchKernelGGL(pad_rows_kernel, dim3(blocks), dim3(256), 0, s, g->desc.slot_mapping,
                            g->desc.context_lens, batch, n);

@@ -9,8 +9,13 @@
 // 1e-10, argmax).  "同一个 Qwen3，两种写法", section 3.6: the fused add + norm
 // moves 32 KiB per 4096-wide bf16 token (read x, residual; write y, residual).
 //
-// All three are HBM-streaming kernels: 16-byte vector loads and stores, fp32
-// math in registers, one pass over memory.
+// Add + RMSNorm and SiluAndMul are HBM-streaming kernels: 16-byte vector loads
+// and stores, fp32 math in registers, one pass over memory.  The sampler also
+// reads each logit once, but with its noise drawn in the kernel (Philox4x32-10:
+// twenty 32x32->64-bit products per four tokens, two logarithms per token) it
+// is bound by vector-ALU issue, not by memory: each row is split over several
+// workgroups so the chip holds enough waves to keep the ALUs busy, and the
+// partial winners meet through a 64-bit atomic maximum on the row's output slot.
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -169,18 +174,6 @@ __device__ __forceinline__ float log2_noise_from_bits(uint32_t bits) {
 //   = (l_i / T) * log2(e) - log2(E_i).
 // The row's softmax normaliser is common to every token, so the argmax needs
 // neither the max nor the sum.  Ties keep the lower index.
-struct Best {
-    float s;
-    int32_t i;
-};
-
-__device__ __forceinline__ void take(Best& b, float s, int32_t i) {
-    if (s > b.s || (s == b.s && i < b.i)) {
-        b.s = s;
-        b.i = i;
-    }
-}
-
 template <bool F32>
 __device__ __forceinline__ void load8(const void* row, int64_t c8, float (&l)[8]) {
     if (F32) {
@@ -202,23 +195,39 @@ __device__ __forceinline__ void load8(const void* row, int64_t c8, float (&l)[8]
     }
 }
 
-constexpr int kSampThreads = 512;
+constexpr int kSampThreads = 256;
 
+// A (score, index) pair as one unsigned 64-bit key whose unsigned order is the
+// argmax order with ties to the lower index: the score's bits made monotone in
+// the high word, the index complemented in the low word.  0 means "nothing
+// taken" (every score NaN); no real pair maps to it.
+__device__ __forceinline__ unsigned long long sample_key(float s, int32_t i) {
+    const uint32_t u = __float_as_uint(s);
+    const uint32_t m = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)m << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)i);
+}
+
+// Each row is split over `parts` workgroups; each reduces its share to one key
+// and folds it into tokens[b] (cleared to 0 by sample_clear_kernel) with a 64-bit
+// atomicMax; sample_finish_kernel turns the key back into the token index.
 template <bool F32>
 __global__ void __launch_bounds__(kSampThreads) sample_gumbel_kernel(
     const void* __restrict__ logits, int64_t row_stride, const float* __restrict__ temperatures,
     const float* __restrict__ noise, int64_t noise_row_stride, uint32_t k0, uint32_t k1, uint32_t off_lo,
-    uint32_t off_hi, int64_t* __restrict__ tokens, int32_t vocab) {
-    __shared__ float s_s[kSampThreads / 64];
-    __shared__ int32_t s_i[kSampThreads / 64];
-    const int b = blockIdx.x, tid = threadIdx.x;
+    uint32_t off_hi, unsigned long long* __restrict__ keys, int32_t vocab, int32_t parts) {
+    __shared__ unsigned long long s_k[kSampThreads / 64];
+    const int b = blockIdx.x / parts, part = blockIdx.x - b * parts, tid = threadIdx.x;
     const float T = fmaxf(temperatures[b], 1e-10f);
     const float mul = 1.4426950408889634f / T;  // log2(e) / T
     const char* row = (const char*)logits + (int64_t)b * row_stride * (F32 ? 4 : 2);
     const float* nrow = noise ? noise + (int64_t)b * noise_row_stride : nullptr;
-    Best best{-INFINITY, 0x7FFFFFFF};
+    // This lane's indices only grow, so a strict > keeps the lowest index among equal scores.
+    float best_s = -INFINITY;
+    int32_t best_i = 0x7FFFFFFF;
     const int64_t n8 = vocab >> 3;
-    for (int64_t c = tid; c < n8; c += kSampThreads) {
+    const int64_t per = (n8 + parts - 1) / parts;
+    const int64_t c0 = part * per, c1 = c0 + per < n8 ? c0 + per : n8;
+    for (int64_t c = c0 + tid; c < c1; c += kSampThreads) {
         float l[8];
         load8<F32>(row, c, l);
         float ln[8];
@@ -241,36 +250,57 @@ __global__ void __launch_bounds__(kSampThreads) sample_gumbel_kernel(
             }
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) take(best, l[e] * mul - ln[e], (int32_t)(8 * c + e));
-    }
-    // tail of a vocab that is not a multiple of 8
-    for (int32_t i = (int32_t)(n8 << 3) + tid; i < vocab; i += kSampThreads) {
-        const float l = F32 ? ((const float*)row)[i] : bf16lo(((const uint16_t*)row)[i]);
-        float ln;
-        if (nrow) {
-            ln = __builtin_amdgcn_logf(fmaxf(nrow[i], 1e-10f));
-        } else {
-            const Philox4 r = philox4x32_10((uint32_t)(i >> 2), (uint32_t)b, off_lo, off_hi, k0, k1);
-            ln = log2_noise_from_bits(r.v[i & 3]);
+        for (int e = 0; e < 8; ++e) {
+            const float sc = l[e] * mul - ln[e];
+            const bool win = sc > best_s;
+            best_s = win ? sc : best_s;
+            best_i = win ? (int32_t)(8 * c + e) : best_i;
         }
-        take(best, l * mul - ln, i);
     }
+    // tail of a vocab that is not a multiple of 8 (last part only)
+    if (part == parts - 1) {
+        for (int32_t i = (int32_t)(n8 << 3) + tid; i < vocab; i += kSampThreads) {
+            const float l = F32 ? ((const float*)row)[i] : bf16lo(((const uint16_t*)row)[i]);
+            float ln;
+            if (nrow) {
+                ln = __builtin_amdgcn_logf(fmaxf(nrow[i], 1e-10f));
+            } else {
+                const Philox4 r = philox4x32_10((uint32_t)(i >> 2), (uint32_t)b, off_lo, off_hi, k0, k1);
+                ln = log2_noise_from_bits(r.v[i & 3]);
+            }
+            const float sc = l * mul - ln;
+            const bool win = sc > best_s;
+            best_s = win ? sc : best_s;
+            best_i = win ? i : best_i;
+        }
+    }
+    unsigned long long key = best_i == 0x7FFFFFFF ? 0ull : sample_key(best_s, best_i);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
-        const float s = __shfl_xor(best.s, o, 64);
-        const int32_t i = __shfl_xor(best.i, o, 64);
-        take(best, s, i);
+        const unsigned long long k2 = __shfl_xor(key, o, 64);
+        key = k2 > key ? k2 : key;
     }
-    if ((tid & 63) == 0) {
-        s_s[tid >> 6] = best.s;
-        s_i[tid >> 6] = best.i;
-    }
+    if ((tid & 63) == 0) s_k[tid >> 6] = key;
     __syncthreads();
     if (tid == 0) {
-        Best r{s_s[0], s_i[0]};
-        for (int w = 1; w < kSampThreads / 64; ++w) take(r, s_s[w], s_i[w]);
-        // every score NaN (NaN logits): fall back to token 0
-        tokens[b] = r.i == 0x7FFFFFFF ? 0 : r.i;
+        unsigned long long r = s_k[0];
+        for (int w = 1; w < kSampThreads / 64; ++w) r = s_k[w] > r ? s_k[w] : r;
+        if (r != 0ull) atomicMax(keys + b, r);
+    }
+}
+
+__global__ void sample_clear_kernel(unsigned long long* __restrict__ keys, int32_t n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) keys[i] = 0ull;
+}
+
+// key -> token index; a row whose every score was NaN (key 0) gets token 0
+__global__ void sample_finish_kernel(unsigned long long* __restrict__ keys, int32_t n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        const unsigned long long k = keys[i];
+        const int64_t tok = k == 0ull ? 0 : (int64_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+        reinterpret_cast<int64_t*>(keys)[i] = tok;
     }
 }
 
@@ -323,12 +353,26 @@ hipError_t launch_sample_gumbel(const void* logits, int64_t row_stride, int32_t 
     if (num_rows == 0) return hipSuccess;
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
     const uint32_t o0 = (uint32_t)offset, o1 = (uint32_t)(offset >> 32);
+    // Enough workgroups to fill the chip (about 2048), at least 16 chunks of 8 per lane pass.
+    const int64_t n8 = vocab >> 3;
+    int64_t parts = (2048 + num_rows - 1) / num_rows;
+    const int64_t max_parts = n8 / (16 * kSampThreads) > 1 ? n8 / (16 * kSampThreads) : 1;
+    if (parts > max_parts) parts = max_parts;
+    if (parts < 1) parts = 1;
+    const int64_t grid = (int64_t)num_rows * parts;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    unsigned long long* keys = reinterpret_cast<unsigned long long*>(tokens);
+    const unsigned nb = (unsigned)((num_rows + 255) / 256);
+    hipLaunchKernelGGL(sample_clear_kernel, dim3(nb), dim3(256), 0, stream, keys, num_rows);
     if (logits_f32)
-        hipLaunchKernelGGL(sample_gumbel_kernel<true>, dim3(num_rows), dim3(kSampThreads), 0, stream, logits,
-                           row_stride, temperatures, noise, noise_row_stride, k0, k1, o0, o1, tokens, vocab);
+        hipLaunchKernelGGL(sample_gumbel_kernel<true>, dim3((unsigned)grid), dim3(kSampThreads), 0, stream, logits,
+                           row_stride, temperatures, noise, noise_row_stride, k0, k1, o0, o1, keys, vocab,
+                           (int32_t)parts);
     else
-        hipLaunchKernelGGL(sample_gumbel_kernel<false>, dim3(num_rows), dim3(kSampThreads), 0, stream, logits,
-                           row_stride, temperatures, noise, noise_row_stride, k0, k1, o0, o1, tokens, vocab);
+        hipLaunchKernelGGL(sample_gumbel_kernel<false>, dim3((unsigned)grid), dim3(kSampThreads), 0, stream, logits,
+                           row_stride, temperatures, noise, noise_row_stride, k0, k1, o0, o1, keys, vocab,
+                           (int32_t)parts);
+    hipLaunchKernelGGL(sample_finish_kernel, dim3(nb), dim3(256), 0, stream, keys, num_rows);
     return hipGetLastError();
 }
 

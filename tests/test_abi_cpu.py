@@ -172,7 +172,7 @@ def _desc(**kw):
                            num_blocks=64, positions=0x6000, slot_mapping=0x7000, context_lens=0x8000,
                            block_table=0x9000, max_blocks_per_seq=8, max_batch=32, q_norm_weight=0xa000,
                            k_norm_weight=0xb000, cos_sin_cache=0xc000, max_position=40960, eps=1e-6, num_q_heads=32,
-                           num_kv_heads=8, head_dim=128, block_size=256, softmax_scale=0.088, reserved=0,
+                           num_kv_heads=8, head_dim=128, block_size=256, softmax_scale=0.088, flags=0,
                            workspace=0x100000, workspace_bytes=1 << 30)
     for k, v in kw.items():
         setattr(d, k, v)

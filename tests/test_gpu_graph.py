@@ -62,14 +62,15 @@ class _Sequences:
         return qkv, pos.astype(np.int64), slots, ctx_i32
 
 
-@pytest.mark.parametrize("hq,hkv,max_batch,max_ctx,batches", [
-    (32, 8, 32, 1000, [3, 32, 17, 1, 9, 5]),
-    (16, 8, 32, 1000, [3, 32, 17, 1, 9, 5]),
-    (32, 8, 512, 256, [512, 300, 257, 1, 129]),     # the whole ladder 1 ... 512, batches past a bucket edge
+@pytest.mark.parametrize("hq,hkv,max_batch,max_ctx,batches,caller_pads", [
+    (32, 8, 32, 1000, [3, 32, 17, 1, 9, 5], False),
+    (16, 8, 32, 1000, [3, 32, 17, 1, 9, 5], False),
+    (32, 8, 512, 256, [512, 300, 257, 1, 129], False),   # the whole ladder 1 ... 512, batches past a bucket edge
+    (32, 8, 32, 1000, [3, 32, 17, 1, 9, 5], True),       # the caller pads rows [b, bucket); no padding launch
 ])
-def test_decode_graph_replays_match_eager_and_oracle(dev, hq, hkv, max_batch, max_ctx, batches):
+def test_decode_graph_replays_match_eager_and_oracle(dev, hq, hkv, max_batch, max_ctx, batches, caller_pads):
     shape = wl.QWEN3_8B if hq == 32 else wl.QWEN3_0_6B
-    _say(f"decode graph {hq}/{hkv} heads, max_batch {max_batch}, batches {batches}")
+    _say(f"decode graph {hq}/{hkv} heads, max_batch {max_batch}, batches {batches}, caller pads: {caller_pads}")
     seqs = _Sequences(max_batch, max_ctx, len(batches), seed=hq + max_batch)
     rng = wl.rng_for(94, hq, 0)
     pool0 = wl.normal_bf16(rng, (2, seqs.num_blocks, 256, hkv, D))
@@ -86,7 +87,7 @@ def test_decode_graph_replays_match_eager_and_oracle(dev, hq, hkv, max_batch, ma
                     ctx=torch.zeros(max_batch, dtype=torch.int32, device=dev),
                     bt=to_dev(seqs.block_tables, dev))
         st = pkv.DecodeStep(bufs["qkv"], bufs["kc"], bufs["vc"], bufs["pos"], bufs["slot"], bufs["ctx"], bufs["bt"],
-                            gq_d, gk_d, table_d, hq, hkv, eps=shape.eps)
+                            gq_d, gk_d, table_d, hq, hkv, eps=shape.eps, caller_pads=caller_pads)
         return st, bufs
 
     graph, gb = make()
@@ -100,13 +101,14 @@ def test_decode_graph_replays_match_eager_and_oracle(dev, hq, hkv, max_batch, ma
         n = graph.bucket(b)
         assert n == next(x for x in graph.buckets if x >= b)
         qkv, pos, slots, ctx = seqs.step_inputs(k, shape, max_batch, b)
-        # graph: junk rows as given, the launch pads them
-        for buf, x in ((gb["qkv"], qkv), (gb["pos"], pos), (gb["slot"], slots), (gb["ctx"], ctx)):
+        ps, pc = slots.copy(), ctx.copy()
+        ps[b:n], pc[b:n] = -1, 0
+        # graph: junk rows as given and the launch pads them, or the caller pads them
+        for buf, x in ((gb["qkv"], qkv), (gb["pos"], pos), (gb["slot"], ps if caller_pads else slots),
+                       (gb["ctx"], pc if caller_pads else ctx)):
             buf.copy_(to_dev(x, dev))
         graph.replay(b)
         # eager at the bucket size with the padding written by the test
-        ps, pc = slots.copy(), ctx.copy()
-        ps[b:n], pc[b:n] = -1, 0
         for buf, x in ((eb["qkv"], qkv), (eb["pos"], pos), (eb["slot"], ps), (eb["ctx"], pc)):
             buf.copy_(to_dev(x, dev))
         eager.run(n)

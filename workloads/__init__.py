@@ -361,6 +361,17 @@ def paged_decode_8b(seed: int = 0, batch: int = 256, lo: int = 1024, hi: int = 3
                        shared_seqs=shared_seqs, shared_blocks=shared, seed=seed)
 
 
+def short_decode_8b(seed: int = 0, batch: int = 64, lo: int = 256, hi: int = 1024) -> PagedDecode:
+    """Qwen3-8B-shaped decode over short contexts (U[lo, hi] tokens): the regime in which
+    a decode step's kernel launches, not its K/V bytes, set the time."""
+    shape = QWEN3_8B
+    ctx = rng_for(6, seed, 0).integers(lo, hi + 1, size=batch).astype(np.int32)
+    mb = blocks_needed(hi, shape.block_size)
+    nb, bt, shared = _decode_pool(6, seed, ctx, shape, [], 0, mb)
+    return PagedDecode(config_id=6, shape=shape, context_lens=ctx, num_blocks=nb, block_tables=bt,
+                       shared_seqs=np.array([], dtype=np.int64), shared_blocks=shared, seed=seed)
+
+
 # ----------------------------------------------------------------------------
 # Workload 5: Qwen3-8B prefill over a cached shared prefix
 # ----------------------------------------------------------------------------
