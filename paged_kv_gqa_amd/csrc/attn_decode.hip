@@ -19,7 +19,7 @@
 //   * A one-workgroup kernel first sorts the split items by size (counting
 //     sort), and workgroups take them largest first: with contexts of very
 //     different lengths the last workgroups to start are the smallest, so the
-//     tail stays short.
+//     tail stays short.  A grid that fits the chip at once skips the sort.
 //   * Loads run one 16-key chunk ahead in a register ring.
 //   * Both products on MFMA.  Scores: v_mfma_f32_16x16x32_bf16 with A = 16 keys
 //     x 32 dims straight from global memory and B = the group's q vectors
@@ -123,8 +123,10 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
     float* __restrict__ part_o, float* __restrict__ part_ml, const int32_t* __restrict__ work) {
     static_assert(G >= 1 && G <= 16, "GQA group must fit the 16 MFMA columns");
     // Dispatch order: split items by decreasing size (full splits first), so the
-    // smallest pieces of work come last and the tail stays short.
-    const int item = work[(int64_t)blockIdx.z * gridDim.y + blockIdx.y];
+    // smallest pieces of work come last and the tail stays short.  Without an
+    // order (a grid small enough to run all at once) the item is the grid position.
+    const int item = work ? work[(int64_t)blockIdx.z * gridDim.y + blockIdx.y]
+                          : (int)blockIdx.y * max_splits + (int)blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // Each wave owns one kv head of a group of 4 (the 4 waves read adjacent 256-byte
     // pieces of every 2 KiB cache row) and streams the whole split for it.
@@ -423,15 +425,21 @@ hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t stream) {
     const int sb = decode_split_blocks(a.num_seqs, a.hkv, a.max_blocks);
     const int ms = (a.max_blocks + sb - 1) / sb;
     Workspace w = carve(a.workspace, a.num_seqs, a.hq, ms);
-    hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(1024), 0, stream, a.context_lens, a.max_blocks, a.num_seqs,
-                       sb, ms, w.work);
     dim3 grid((a.hkv + 3) / 4, a.num_seqs, ms);
+    // The size-ordered dispatch pays when workgroups queue for the chip; when the
+    // whole grid fits at once (two split workgroups per CU, 256 CUs) the order kernel
+    // is skipped: one launch less on short, small-batch steps.
+    const bool ordered = (int64_t)grid.x * grid.y * grid.z > 512;
+    if (ordered)
+        hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(1024), 0, stream, a.context_lens, a.max_blocks,
+                           a.num_seqs, sb, ms, w.work);
+    const int32_t* work = ordered ? w.work : nullptr;
 #define PKV_DECODE_CASE(GG)                                                                                       \
     case GG:                                                                                                      \
         hipLaunchKernelGGL(decode_split_kernel<GG>, grid, dim3(kDecThreads), 0, stream, (const uint16_t*)a.q,     \
                            (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.context_lens, a.block_table, \
                            a.max_blocks, a.hq, a.hkv, a.num_blocks, a.scale_log2, sb, ms, w.part_o, w.part_ml,   \
-                           w.work);                                                                               \
+                           work);                                                                                 \
         break;
     switch (G) {
         PKV_DECODE_CASE(1)

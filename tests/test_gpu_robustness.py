@@ -296,11 +296,10 @@ def test_single_rounding_against_the_pages_rounding_points(dev):
     pk = oracle.rmsnorm_rope(w.qkv, 8, D, w.gamma_k, s.eps, w.positions, th, col_offset=k0, pages_rounding=True)
     exact_q = oracle.rmsnorm_rope(w.qkv, 16, D, w.gamma_q, s.eps, w.positions, th, col_offset=q0)
     diff_frac = float(np.mean(np.concatenate([(gq != pq).ravel(), (gk != pk).ravel()])))
-    step = np.exp2(np.floor(np.log2(np.maximum(np.abs(exact_q), 2.0 ** -126))) - 7)
     pair = np.sqrt(exact_q[..., :64] ** 2 + exact_q[..., 64:] ** 2)
     pair_step = np.exp2(np.floor(np.log2(np.maximum(np.concatenate([pair, pair], -1), 2.0 ** -126))) - 7)
-    err_k = np.abs(gq - exact_q)
-    err_p = np.abs(pq - exact_q)
+    err_k = np.abs(gq - exact_q) / pair_step     # in bf16 steps of the rotated pair's length
+    err_p = np.abs(pq - exact_q) / pair_step
     assert np.all(np.abs(gq - pq) <= 4 * pair_step), "single rounding and the pages' three differ by > 4 steps"
     vb = np.ascontiguousarray(w.qkv[:, v0:]).reshape(n, 8, D)
     ref = oracle.attn_prefill(oracle.round_bf16(exact_q), oracle.round_bf16(
@@ -314,7 +313,7 @@ def test_single_rounding_against_the_pages_rounding_points(dev):
     mx_p, mean_p = check_attn(o_pages, ref, "attention over the pages-rounded q', k'")
     gap = np.abs(f64(o_gpu) - o_pages)
     _say(f"q'/k': {diff_frac:.4f} of values differ between single rounding and the pages' three; "
-         f"|q'-exact| in steps of the value: kernel max {np.max(err_k / step):.2f} mean {np.mean(err_k / step):.3f}, "
-         f"pages max {np.max(err_p / step):.2f} mean {np.mean(err_p / step):.3f}; attention vs oracle: kernel "
+         f"|q'-exact| in bf16 steps of the pair length: kernel max {np.max(err_k):.2f} mean {np.mean(err_k):.3f}, "
+         f"pages max {np.max(err_p):.2f} mean {np.mean(err_p):.3f}; attention vs oracle: kernel "
          f"{mx_g:.2e}/{mean_g:.2e}, pages pipeline {mx_p:.2e}/{mean_p:.2e}; kernel vs pages pipeline "
          f"{gap.max():.2e}/{gap.mean():.2e}")
