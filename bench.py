@@ -69,18 +69,24 @@ def gpu_lead(torch, ms: float):
 
 
 def input_checksum(torch, named):
-    """sha256 (first 16 hex digits) over each input's name, shape, dtype and the sum of its
-    32-bit words (device reduction in 64 MiB pieces, int64 accumulate).  Recorded with the
-    seed so a run's synthetic inputs can be told apart from another's."""
+    """sha256 (first 16 hex digits) over each input's name, shape, dtype, the sum of its
+    32-bit words and their position-weighted sum (word i times (i * 2654435761) mod 2^32,
+    int64 arithmetic wrapping mod 2^64; device reduction in 16M-word pieces).  Recorded with
+    the seed so a run's synthetic inputs can be told apart from another's; the weighted sum
+    also tells a permuted block table or slot map from the original."""
     import hashlib
     h = hashlib.sha256()
     for name, t in named:
         flat = t.reshape(-1).view(torch.int32) if t.element_size() * t.numel() % 4 == 0 else t.reshape(-1)
-        total = 0
+        total = weighted = 0
         step = 1 << 24
         for i in range(0, flat.numel(), step):
-            total += int(torch.sum(flat[i:i + step], dtype=torch.int64).item())
-        h.update(f"{name}:{tuple(t.shape)}:{t.dtype}:{total};".encode())
+            piece = flat[i:i + step].to(torch.int64)
+            idx = torch.arange(i, i + piece.numel(), dtype=torch.int64, device=piece.device)
+            w = (idx * 2654435761) & 0xFFFFFFFF
+            total += int(torch.sum(piece).item())
+            weighted = (weighted + int(torch.sum(piece * w).item())) % (1 << 64)
+        h.update(f"{name}:{tuple(t.shape)}:{t.dtype}:{total}:{weighted};".encode())
     return h.hexdigest()[:16]
 
 

@@ -49,3 +49,13 @@ def test_input_checksum_sees_every_word():
         assert bench.input_checksum(torch, [("a", a2), ("b", b)]) != ref
     assert bench.input_checksum(torch, [("a", a), ("b", b + 1)]) != ref
     assert bench.input_checksum(torch, [("b", b), ("a", a)]) != ref
+    # a permutation keeps the plain sum but not the position-weighted one
+    for i, j in ((0, 1), (5, 5 + (1 << 16)), (7, b.numel() - 1)):
+        if j >= b.numel():
+            continue
+        b2 = b.clone()
+        b2[i], b2[j] = b[j], b[i]
+        assert bench.input_checksum(torch, [("a", a), ("b", b2)]) != ref
+    a3 = a.clone().view(torch.int32)
+    a3[[3, 1000]] = a3[[1000, 3]]
+    assert bench.input_checksum(torch, [("a", a3.view(torch.bfloat16)), ("b", b)]) != ref
