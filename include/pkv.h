@@ -7,6 +7,7 @@
  *   pkv_qk_norm_rope         per-head RMSNorm of q and k, then RoPE
  *   pkv_store_kvcache        scatter of k and v rows into the paged KV cache
  *   pkv_attn_prefill_varlen  varlen causal GQA prefill (fresh K/V or paged)
+ *   pkv_attn_prefill_workspace_bytes  its optional key-split workspace
  *   pkv_attn_decode_paged    single-token paged decode
  *
  * plus pkv_rope_cache_build, which fills the cos/sin table once at set-up,
@@ -193,11 +194,23 @@ PKV_API int pkv_qk_norm_rope_store(const void* q, int64_t q_row_stride, const vo
  * Sequences with Lq_b == 0 contribute nothing.  Output rows are written in
  * full for every query row.
  *
+ *   workspace, workspace_bytes
+ *                     optional device scratch (NULL, 0: none), 256-byte aligned,
+ *                     not overlapping any other argument.  When it holds at least
+ *                     pkv_attn_prefill_workspace_bytes(...) (> 0) bytes, a batch
+ *                     with few query blocks and long key ranges splits each long
+ *                     block's keys over several workgroups and adds their partial
+ *                     sums in a fixed order; otherwise the call runs unsplit.  The
+ *                     two differ only in fp32 summation order.  Contents on entry
+ *                     do not matter; the call owns the bytes until its work on
+ *                     `stream` completes.
+ *
  * Large batches run as two kernels on `stream`: a fast pass, then a pass that
  * recomputes any work item whose softmax sums left the fast pass's range (until
  * then such rows of o hold a marker value, so o is complete only when the call's
- * work on `stream` is).  The library keeps one 8-byte device word per GPU for
- * this; calls on several streams may overlap, and a call may be captured into a
+ * work on `stream` is); a split call adds a merge kernel between them.  The
+ * library keeps one 8-byte device word per GPU for this; calls on several streams
+ * may overlap (each with its own workspace), and a call may be captured into a
  * HIP graph and replayed.
  */
 PKV_API int pkv_attn_prefill_varlen(const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride,
@@ -205,7 +218,18 @@ PKV_API int pkv_attn_prefill_varlen(const void* q, int64_t q_row_stride, const v
                             const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
                             int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                             float softmax_scale, int32_t causal, const int32_t* block_table,
-                            int32_t max_blocks_per_seq, int32_t block_size, int64_t num_blocks, void* stream);
+                            int32_t max_blocks_per_seq, int32_t block_size, int64_t num_blocks, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_attn_prefill_workspace_bytes -- workspace pkv_attn_prefill_varlen splits
+ * key ranges with for a call of these sizes (arguments as there); 0 when such a
+ * call does not split (many query blocks, short keys, or invalid sizes).  At
+ * most 512 MiB.
+ */
+PKV_API size_t pkv_attn_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                                                int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads,
+                                                int32_t head_dim);
 
 /*
  * pkv_attn_decode_workspace_bytes -- device workspace pkv_attn_decode_paged

@@ -40,7 +40,7 @@ _STATUS = {-1: "invalid argument", -2: "unsupported", -3: "launch failed", -4: "
 
 #: every symbol include/pkv.h declares
 EXPORTED = ("pkv_last_error", "pkv_version", "pkv_rope_cache_build", "pkv_qk_norm_rope",
-            "pkv_qk_norm_rope_store", "pkv_store_kvcache", "pkv_attn_prefill_varlen",
+            "pkv_qk_norm_rope_store", "pkv_store_kvcache", "pkv_attn_prefill_varlen", "pkv_attn_prefill_workspace_bytes",
             "pkv_attn_decode_workspace_bytes", "pkv_attn_decode_paged", "pkv_decode_step_workspace_bytes",
             "pkv_decode_step", "pkv_decode_graph_create", "pkv_decode_graph_bucket", "pkv_decode_graph_launch",
             "pkv_decode_graph_destroy", "pkv_add_rms_norm", "pkv_silu_and_mul", "pkv_sample_gumbel",
@@ -99,8 +99,10 @@ def load_library(path: str = LIB_PATH):
     lib.pkv_store_kvcache.argtypes = [P, I64, P, I64, P, P, I64, P, I32, I32, I32, I32, P]
     lib.pkv_store_kvcache.restype = ctypes.c_int
     lib.pkv_attn_prefill_varlen.argtypes = [P, I64, P, I64, P, I64, P, P, P, I32, I32, I32, I32, I32, I32, I32,
-                                            F32, I32, P, I32, I32, I64, P]
+                                            F32, I32, P, I32, I32, I64, P, SZ, P]
     lib.pkv_attn_prefill_varlen.restype = ctypes.c_int
+    lib.pkv_attn_prefill_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
+    lib.pkv_attn_prefill_workspace_bytes.restype = SZ
     lib.pkv_attn_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
     lib.pkv_attn_decode_workspace_bytes.restype = SZ
     lib.pkv_attn_decode_paged.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I64, F32, P, SZ, P]
@@ -305,11 +307,21 @@ def store_kvcache(key, value, k_cache, v_cache, slot_mapping, stream=None):
                                  _ptr(slot_mapping), n, hkv, HEAD_DIM, key.element_size(), _stream(stream)))
 
 
+def prefill_workspace_bytes(num_seqs: int, total_q: int, max_seqlen_q: int, max_seqlen_k: int, num_q_heads: int,
+                            num_kv_heads: int) -> int:
+    """Bytes of the optional key-split workspace of a prefill call of these sizes (0: no split)."""
+    return int(load_library().pkv_attn_prefill_workspace_bytes(num_seqs, total_q, int(max_seqlen_q),
+                                                               int(max_seqlen_k), num_q_heads, num_kv_heads,
+                                                               HEAD_DIM))
+
+
 def attn_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
                         softmax_scale: Optional[float] = None, causal: bool = True, block_table=None, out=None,
-                        stream=None):
+                        workspace=None, stream=None):
     """Varlen causal GQA prefill.  q: [Tq, Hq, 128]; k/v: [Tk, Hkv, 128] (case 1) or the caches
-    [num_blocks, 256, Hkv, 128] with block_table [B, max_blocks] (case 2).  Returns o [Tq, Hq, 128]."""
+    [num_blocks, 256, Hkv, 128] with block_table [B, max_blocks] (case 2).  Returns o [Tq, Hq, 128].
+    workspace: a uint8 device tensor for the key split (None: allocated here when the call
+    would split; an empty tensor: run unsplit)."""
     import torch
     lib = load_library()
     tq, hq = q.shape[0], q.shape[1]
@@ -339,11 +351,19 @@ def attn_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, 
     if out is None:
         out = torch.empty((tq, hq, HEAD_DIM), dtype=torch.bfloat16, device=q.device)
     _out(out, (tq, hq, HEAD_DIM), q, "out")
+    if workspace is None:
+        need = prefill_workspace_bytes(nseq, tq, max_seqlen_q, max_seqlen_k, hq, hkv)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    elif workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    else:
+        _same_device(q, workspace=workspace)
+    ws_ptr, ws_bytes = (_ptr(workspace), workspace.numel()) if workspace is not None and workspace.numel() else (None, 0)
     _check("pkv_attn_prefill_varlen",
            lib.pkv_attn_prefill_varlen(_ptr(q), qs, _ptr(k), ks, _ptr(v), vs, _ptr(out), _ptr(cu_seqlens_q),
                                        _ptr(cu_seqlens_k), nseq, tq, int(max_seqlen_q), int(max_seqlen_k), hq, hkv,
                                        HEAD_DIM, float(scale), 1 if causal else 0, _ptr(block_table), mb,
-                                       BLOCK_SIZE, num_blocks, _stream(stream)))
+                                       BLOCK_SIZE, num_blocks, ws_ptr, ws_bytes, _stream(stream)))
     return out
 
 

@@ -182,7 +182,8 @@ int pkv_attn_prefill_varlen(const void* q, int64_t q_row_stride, const void* k, 
                             const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
                             int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                             float softmax_scale, int32_t causal, const int32_t* block_table,
-                            int32_t max_blocks_per_seq, int32_t block_size, int64_t num_blocks, void* stream) {
+                            int32_t max_blocks_per_seq, int32_t block_size, int64_t num_blocks, void* workspace,
+                            size_t workspace_bytes, void* stream) {
     const char* fn = "pkv_attn_prefill_varlen";
     int rc = check_heads(fn, num_q_heads, num_kv_heads, head_dim);
     if (rc) return rc;
@@ -216,6 +217,16 @@ int pkv_attn_prefill_varlen(const void* q, int64_t q_row_stride, const void* k, 
     }
     PKV_REQUIRE(((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) % 16 == 0, PKV_ERR_INVALID_ARG,
                 "%s: tensors must be 16-byte aligned", fn);
+    if (workspace && workspace_bytes) {
+        PKV_REQUIRE((uintptr_t)workspace % 256 == 0, PKV_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned",
+                    fn);
+        // the split writes partial sums while q is read and o written
+        const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + workspace_bytes;
+        const uintptr_t q0 = (uintptr_t)q, q1 = q0 + (uintptr_t)(((int64_t)(total_q - 1) * q_row_stride + qw) * 2);
+        const uintptr_t o0 = (uintptr_t)o, o1 = o0 + (uintptr_t)((int64_t)total_q * qw * 2);
+        PKV_REQUIRE((w1 <= q0 || q1 <= w0) && (w1 <= o0 || o1 <= w0), PKV_ERR_WORKSPACE,
+                    "%s: workspace must not overlap q or o", fn);
+    }
     if (block_table) {
         PKV_REQUIRE(block_size == 256, PKV_ERR_UNSUPPORTED, "%s: block_size %d unsupported (only 256)", fn,
                     block_size);
@@ -247,7 +258,18 @@ int pkv_attn_prefill_varlen(const void* q, int64_t q_row_stride, const void* k, 
     a.block_table = block_table;
     a.max_blocks = block_table ? max_blocks_per_seq : 0;
     a.num_blocks = block_table ? num_blocks : 0;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace ? workspace_bytes : 0;
     return launched(pkv::launch_attn_prefill(a, (hipStream_t)stream), fn);
+}
+
+size_t pkv_attn_prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                                        int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim) {
+    if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < max_seqlen_q || num_q_heads <= 0 ||
+        num_kv_heads <= 0 || num_q_heads % num_kv_heads || head_dim != 128)
+        return 0;
+    return pkv::prefill_workspace_bytes(num_seqs, total_q, max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads);
 }
 
 size_t pkv_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

@@ -83,12 +83,69 @@ constexpr int kTileKeys = NW == 8 ? 128 : 64;
 // to bf16 can have (those NaNs are quiet).
 constexpr uint16_t kFixupMarker = 0x7F81;
 constexpr bf16x2 kOnes2 = {(bf16)1.0f, (bf16)1.0f};
+// Key split: every chunk of a split work item holds at least this many tiles.
+constexpr int kSplitMinChunkTiles = 8;
+// Floats one wave leaves per chunk of a split item: its 64 O^T accumulators per
+// lane (entry 64 * r + lane) and its partial row sum per lane.
+constexpr int kPartFloats = 64 * 64 + 64;
+constexpr size_t kSplitMaxBytes = size_t(512) << 20;
 }  // namespace
+
+// Chunks of a work item of n_tiles key tiles when the call splits items into up to
+// nc chunks: 1 (no split) below 2 * kSplitMinChunkTiles tiles.
+__host__ __device__ inline int item_chunks(int n_tiles, int nc) {
+    return nc > 1 && n_tiles >= 2 * kSplitMinChunkTiles ? min(nc, n_tiles / kSplitMinChunkTiles) : 1;
+}
 
 // Highest call number (see launch_attn_prefill) whose fast pass flagged a work
 // item; raised with a device-scope atomic, never lowered.  The exact pass of a
 // call scans for markers only when this is at least its own number.
 __device__ unsigned long long g_prefill_flagged_call = 0;
+
+// End of a wave's 32 query rows of one head: lane holds O^T[d][qi] for
+// d = 32dt + 8(r/4) + 4*h32 + r%4 and its part of the row sum.  kCheck (fast
+// pass): did every live row stay inside the fast pass's range?  l in [2^-64, 2^64]
+// bounds every weight and keeps the row clear of underflow; a finite sum of this
+// lane's O entries means no product overflowed.  If not, the wave leaves
+// kFixupMarker in its first output element instead of its results, and the exact
+// pass recomputes the whole work item.  Otherwise: normalise and store.
+template <bool kCheck>
+__device__ __forceinline__ void prefill_finish(const PrefillArgs& a, uint64_t call, int cq0, int Lq, int wp0,
+                                               int head, bool wave_live, const f32x16 (&oacc)[4], float l_part) {
+    const int lane = __lane_id();
+    const float l = l_part + __shfl_xor(l_part, 32, 64);
+    if (kCheck) {
+        float osum = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) osum += oacc[dt][r];
+        const bool row_bad = wave_live && !(l >= 0x1p-64f && l <= 0x1p64f && osum - osum == 0.f);
+        if (__any(row_bad)) {
+            if (lane == 0) {
+                *((uint16_t*)a.o + ((int64_t)(cq0 + wp0) * a.hq + head) * kHeadDim) = kFixupMarker;
+                atomicMax(&g_prefill_flagged_call, (unsigned long long)call);
+            }
+            return;
+        }
+    }
+    const int qi = wp0 + (lane & 31), h32 = lane >> 5;
+    if (!wave_live || qi >= Lq) return;
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const int orow = cq0 + qi;
+    if (orow >= a.total_q) return;
+    uint16_t* op = (uint16_t*)a.o + ((int64_t)orow * a.hq + head) * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int d = 32 * dt + 8 * r4 + 4 * h32;
+            u32x2 w;
+            w[0] = pack_bf16x2(oacc[dt][4 * r4] * inv, oacc[dt][4 * r4 + 1] * inv);
+            w[1] = pack_bf16x2(oacc[dt][4 * r4 + 2] * inv, oacc[dt][4 * r4 + 3] * inv);
+            *reinterpret_cast<u32x2*>(op + d) = w;
+        }
+}
 
 // One work item: query block mb of (sequence b, kv head g, head group hg), with
 // NW waves (4 or 8; two waves per SIMD either way: two workgroups of 4 per CU,
@@ -96,7 +153,8 @@ __device__ unsigned long long g_prefill_flagged_call = 0;
 // v_lds3 are the workgroup's tile buffers.
 template <int GW, bool PAGED, int NW, bool kExact>
 __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_blocks, int32_t head_groups,
-                                              int32_t work, lds_byte* k_lds3, lds_byte* v_lds3, uint64_t call) {
+                                              int32_t work, lds_byte* k_lds3, lds_byte* v_lds3, uint64_t call,
+                                              int c = 0, int nc = 1, float* part = nullptr) {
     constexpr int kThreads = 64 * NW;
     constexpr int kKT = kTileKeys<NW>;
     constexpr int kKH = kKT / 32;                       // 32-key blocks per tile
@@ -155,6 +213,12 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
     const int n_tiles = (wg_keys + kKT - 1) / kKT;
     const int wave_keys = wave_live ? off + wq_last + 1 : 0;
     const int wave_tiles = (wave_keys + kKT - 1) / kKT;
+    // Key split (fast pass only): chunk c of the item's nc_item chunks covers key
+    // tiles [t_begin, t_end); a split item leaves partial sums in `part`.
+    const int nc_item = kExact ? 1 : item_chunks(n_tiles, nc);
+    if (c >= nc_item) return;
+    const int t_begin = c * n_tiles / nc_item, t_end = (c + 1) * n_tiles / nc_item;
+    const bool split = nc_item > 1;
 
     // ---- Q^T as the B operand: lane owns query row l%32, dims 8*(l/32) + 16*st .. +7.
     // Q stays as given (bf16): its products with K are exact in the fp32
@@ -368,18 +432,22 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
         bool ok_cur = false;   // fast pass: whether tile t's block id is usable, found when its copies were issued
         int32_t blk_next = 0;  // fast pass: block id of tile t+1
         if (kDma) {
-            const int32_t blk0 = blk_of(0, load_blk(0));
-            blk_next = load_blk(min(1, n_tiles - 1));
-            (void)row0_of(0, blk0, ok_cur);
-            if (tile_full(0, blk0)) { issue_half(0, 0, blk0, false); issue_half(0, 0, blk0, true); }
-            else fill_tile_sync(0, 0, blk0);
+            const int32_t blk0 = blk_of(t_begin, load_blk(t_begin));
+            blk_next = load_blk(min(t_begin + 1, n_tiles - 1));
+            (void)row0_of(t_begin, blk0, ok_cur);
+            if (tile_full(t_begin, blk0)) {
+                issue_half(t_begin, t_begin & 1, blk0, false);
+                issue_half(t_begin, t_begin & 1, blk0, true);
+            } else {
+                fill_tile_sync(t_begin, t_begin & 1, blk0);
+            }
         } else {
             load_tile(0);
             store_tile(0, k_lds, v_lds);
             if (1 < n_tiles) load_tile(1);
             __syncthreads();
         }
-        for (int t = 0; t < n_tiles; ++t) {
+        for (int t = t_begin; t < t_end; ++t) {
             unsigned char* kb = k_lds + (t & 1) * kKTileBytes;
             unsigned char* vb = v_lds + (t & 1) * kVTileBytes;
             if (kDma) {
@@ -392,7 +460,7 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
             bool ok_next = false;
             bool v_later = false;   // V copies of tile t+1 issued after the QK^T phase
             int32_t blk1 = 0;
-            if (kDma && t + 1 < n_tiles) {
+            if (kDma && t + 1 < t_end) {
                 const int32_t blk = blk_of(t + 1, blk_next);
                 blk1 = blk;
                 (void)row0_of(t + 1, blk, ok_next);
@@ -549,48 +617,18 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
         }
     }
 
-    if (!kExact) {
-        // Did every live row of this wave stay inside the fast pass's range?  l in
-        // [2^-64, 2^64] bounds every weight and keeps the row clear of underflow; a
-        // finite sum of this lane's O entries means no product overflowed.  If not,
-        // the wave leaves kFixupMarker in its first output element instead of its
-        // results, and the exact pass recomputes the whole work item.
-        const float l_fast = l_part + __shfl_xor(l_part, 32, 64);
-        float osum = 0.f;
+    if (split) {
+        // this chunk's share: O^T accumulators and row sums, summed by the merge kernel
+        const int lane_e = __lane_id();
+        float* pp = part + ((size_t)(work * nc + c) * NW + (threadIdx.x >> 6)) * kPartFloats;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) osum += oacc[dt][r];
-        const bool row_bad = wave_live && !(l_fast >= 0x1p-64f && l_fast <= 0x1p64f && osum - osum == 0.f);
-        if (__any(row_bad)) {
-            if (lane == 0) {
-                *((uint16_t*)a.o + ((int64_t)(cq0 + wp0) * a.hq + head) * kHeadDim) = kFixupMarker;
-                atomicMax(&g_prefill_flagged_call, (unsigned long long)call);
-            }
-            return;
-        }
+            for (int r = 0; r < 16; ++r) pp[(dt * 16 + r) * 64 + lane_e] = oacc[dt][r];
+        pp[64 * 64 + lane_e] = l_part;
+        return;
     }
-
-    // ---- normalise and store: lane holds O^T[d][qi] for d = 32dt + 8(r/4) + 4*h32 + r%4.
-    // (the lane's row and half are recomputed here rather than kept across the loop)
-    const int lane_e = __lane_id();
-    const int qi_e = wp0 + (lane_e & 31), h32_e = lane_e >> 5;
-    if (!wave_live || qi_e >= Lq) return;
-    const float l = l_part + __shfl_xor(l_part, 32, 64);
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
-    const int orow = cq0 + qi_e;
-    if (orow >= a.total_q) return;
-    uint16_t* op = (uint16_t*)a.o + ((int64_t)orow * a.hq + head) * kHeadDim;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const int d = 32 * dt + 8 * r4 + 4 * h32_e;
-            u32x2 w;
-            w[0] = pack_bf16x2(oacc[dt][4 * r4] * inv, oacc[dt][4 * r4 + 1] * inv);
-            w[1] = pack_bf16x2(oacc[dt][4 * r4 + 2] * inv, oacc[dt][4 * r4 + 3] * inv);
-            *reinterpret_cast<u32x2*>(op + d) = w;
-        }
+    prefill_finish<!kExact>(a, call, cq0, Lq, wp0, head, wave_live, oacc, l_part);
 }
 
 // The two passes are separate kernels so that the exact pass's code does not
@@ -599,7 +637,8 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
 // workgroup per CU slot, which exits at once unless this call flagged something.
 template <int GW, bool PAGED, int NW>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a, int32_t m_blocks, int32_t n_work,
-                                                                  int32_t head_groups, int32_t chunk, uint64_t call) {
+                                                                  int32_t head_groups, int32_t chunk, uint64_t call,
+                                                                  int32_t nc, float* part) {
     constexpr int kKT = kTileKeys<NW>;
     __shared__ __attribute__((aligned(16))) unsigned char k_lds[2 * kKT * kHeadDim * 2];
     __shared__ __attribute__((aligned(16))) unsigned char v_lds[2 * kKT * kHeadDim * 2];
@@ -610,10 +649,74 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a,
     // all its query blocks, so its K/V stays in one L2 -- unless there are fewer
     // units than XCDs; then it is two query blocks, so few sequences still spread
     // over all XCDs.
-    const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
+    //
+    // With a key split (nc > 1) the nc chunks of each item take consecutive slots of
+    // its XCD, so they run side by side and share the item's K/V in one L2.
+    const int xcd = blockIdx.x & 7;
+    int kx = blockIdx.x >> 3, c = 0;
+    if (nc > 1) {
+        c = kx % nc;
+        kx /= nc;
+    }
     const int work = (xcd + 8 * (kx / chunk)) * chunk + kx % chunk;
     if (work >= n_work) return;
-    prefill_block<GW, PAGED, NW, false>(a, m_blocks, head_groups, work, (lds_byte*)k_lds, (lds_byte*)v_lds, call);
+    prefill_block<GW, PAGED, NW, false>(a, m_blocks, head_groups, work, (lds_byte*)k_lds, (lds_byte*)v_lds, call, c,
+                                        nc, part);
+}
+
+
+// Key split: one wave per (work item, 32-row block).  Sums the chunks' partial O^T
+// and row sums in chunk order (deterministic), then finishes as the fast pass does
+// (range check, marker or normalised store).
+template <int GW, bool PAGED, int NW>
+__global__ void __launch_bounds__(64) prefill_merge_kernel(PrefillArgs a, int32_t m_blocks, int32_t n_work,
+                                                           int32_t head_groups, int32_t nc, const float* part,
+                                                           uint64_t call) {
+    constexpr int kKT = kTileKeys<NW>;
+    constexpr int kBM = kRowsPerWave * (NW / GW);
+    const int work = blockIdx.x / NW, wave = blockIdx.x % NW;
+    if (work >= n_work) return;
+    const int mb = m_blocks - 1 - (work % m_blocks);
+    int rest = work / m_blocks;
+    const int hg = rest % head_groups;
+    rest /= head_groups;
+    const int g = rest % a.hkv;
+    const int b = rest / a.hkv;
+    const int cq0 = a.cu_q[b], cq1 = a.cu_q[b + 1];
+    const int ck0 = a.cu_k[b], ck1 = a.cu_k[b + 1];
+    const int Lq = cq1 - cq0, Lk = ck1 - ck0;
+    const int p0 = mb * kBM;
+    if (p0 >= Lq || Lk < Lq || Lq <= 0) return;
+    if (cq0 < 0 || cq1 > a.total_q || ck0 < 0) return;
+    const int off = Lk - Lq;
+    const int n_tiles = (off + min(p0 + kBM, Lq) + kKT - 1) / kKT;
+    const int nc_item = item_chunks(n_tiles, nc);
+    if (nc_item < 2) return;
+    const int lane = threadIdx.x;
+    const int head = g * (a.hq / a.hkv) + hg * GW + (wave % GW);
+    const int wp0 = p0 + kRowsPerWave * (wave / GW);
+    f32x16 oacc[4];
+    float l_part = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+    // each chunk's 65 loads issued together, then added in chunk order
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        if (c >= nc_item) break;
+        const float* pp = part + ((size_t)(work * nc + c) * NW + wave) * kPartFloats;
+        f32x16 t[4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) t[dt][r] = __builtin_nontemporal_load(pp + (dt * 16 + r) * 64 + lane);
+        const float tl = __builtin_nontemporal_load(pp + 64 * 64 + lane);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) oacc[dt] += t[dt];
+        l_part += tl;
+    }
+    prefill_finish<true>(a, call, cq0, Lq, wp0, head, wp0 < Lq, oacc, l_part);
 }
 
 // call != 0: after the fast pass, recompute the work items it flagged (exits at
@@ -639,42 +742,99 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_exact_kernel(PrefillA
     }
 }
 
-hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t stream) {
-    if (a.num_seqs == 0 || a.total_q == 0 || a.max_seqlen_q == 0) return hipSuccess;
-    const int G = a.hq / a.hkv;
-    const int gw = G >= 4 ? 4 : G;                 // query heads per workgroup
-    if (G % gw) return hipErrorInvalidValue;
-    const int head_groups = G / gw;
-    // Four query heads share each K/V tile across 8 waves (64 positions); smaller
-    // groups keep 4 waves so short sequences still spread over many workgroups.
+namespace {
+// Launch shape of a call, shared by the launcher and the workspace query.
+struct PrefillPlan {
+    bool ok = false;
+    int gw = 0, head_groups = 0, nw = 0, m_blocks = 0, n_work = 0, grid = 0, grid_exact = 0, n_iter = 0;
+    int64_t chunk = 0;
+    bool wide = false, two_pass = false;
+    int split_nc = 1;          // chunks per split item (1: no split)
+    size_t split_bytes = 0;    // workspace the split needs
+};
+
+PrefillPlan plan_prefill(int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t hq,
+                         int32_t hkv) {
+    PrefillPlan p;
+    if (num_seqs <= 0 || total_q <= 0 || max_seqlen_q <= 0 || hq <= 0 || hkv <= 0 || hq % hkv) return p;
+    const int G = hq / hkv;
+    p.gw = G >= 4 ? 4 : G;                 // query heads per workgroup
+    if (G % p.gw) return p;
+    p.head_groups = G / p.gw;
     // 8 waves (64 positions x 4 heads, or 128 x 2, 128-key tiles) for long
     // sequences; 4 waves (smaller workgroups, more of them) for short ones
-    const bool wide = gw >= 2 && (int64_t)a.total_q >= (int64_t)2048 * a.num_seqs;
-    const int nw = wide ? 8 : 4;
-    const int bm = kRowsPerWave * (nw / gw);
-    const int m_blocks = (a.max_seqlen_q + bm - 1) / bm;
-    const int64_t n_work64 = (int64_t)a.num_seqs * a.hkv * head_groups * m_blocks;
-    if (n_work64 > (int64_t)0x7FFFFFF0) return hipErrorInvalidValue;
-    const int n_work = (int)n_work64;
+    p.wide = p.gw >= 2 && (int64_t)total_q >= (int64_t)2048 * num_seqs;
+    p.nw = p.wide ? 8 : 4;
+    const int bm = kRowsPerWave * (p.nw / p.gw);
+    p.m_blocks = (max_seqlen_q + bm - 1) / bm;
+    const int64_t n_work64 = (int64_t)num_seqs * hkv * p.head_groups * p.m_blocks;
+    if (n_work64 > (int64_t)0x7FFFFFF0) return p;
+    p.n_work = (int)n_work64;
     // Whole units (all query blocks of a sequence and kv head) per XCD keep their
     // K/V in one L2; with fewer units than XCDs they are cut into 2-block chunks.
-    const int64_t units = n_work64 / m_blocks;
-    const int64_t chunk = units >= 8 ? m_blocks : (m_blocks < 2 ? m_blocks : 2);
-    const int64_t n_chunks = (n_work64 + chunk - 1) / chunk;
-    const int64_t grid64 = ((n_chunks + 7) / 8) * 8 * chunk;
-    if (grid64 > (int64_t)0x7FFFFFF0) return hipErrorInvalidValue;
-    const int grid = (int)grid64;
+    const int64_t units = n_work64 / p.m_blocks;
+    p.chunk = units >= 8 ? p.m_blocks : (p.m_blocks < 2 ? p.m_blocks : 2);
+    const int64_t n_chunks = (n_work64 + p.chunk - 1) / p.chunk;
+    const int64_t grid64 = ((n_chunks + 7) / 8) * 8 * p.chunk;
+    if (grid64 > (int64_t)0x7FFFFFF0 / 4) return p;
+    p.grid = (int)grid64;
     // Batches under 2e10 FLOP (counted without the causal half, so roughly under
     // 20 us of work) run the exact pass alone in one launch: there the second
     // launch of the two-pass scheme (~4 us when nothing is flagged) costs more than
     // the fast pass saves (measured: two passes 10% slower at 16 x 128 tokens,
     // even at 4 x 512, 7-9% faster from 8 x 1024 and on 16 x 2048 queries over
     // 4096 keys).
-    const bool two_pass = (double)a.total_q * a.max_seqlen_k * a.hq * 4.0 * kHeadDim >= 2e10;
+    p.two_pass = (double)total_q * max_seqlen_k * hq * 4.0 * kHeadDim >= 2e10;
     // Exact pass after the fast one: one workgroup per CU slot (two 4-wave or one
     // 8-wave per CU), walking the work items.
-    const int grid_exact = two_pass ? (int)std::min<int64_t>(n_work64, nw == 8 ? 256 : 512) : grid;
-    const int n_iter = two_pass ? n_work : grid;
+    const int slots = p.nw == 8 ? 256 : 512;
+    p.grid_exact = p.two_pass ? (int)std::min<int64_t>(n_work64, slots) : p.grid;
+    p.n_iter = p.two_pass ? p.n_work : p.grid;
+    // Key split: when the items that hold queries (at most one partial query block
+    // per sequence beyond total_q / block) do not fill the CU slots and keys run
+    // long, the fast pass cuts every item of at least 2 * kSplitMinChunkTiles tiles
+    // into slots / items + 1 chunks (2 to 4), whose partial sums a merge kernel
+    // adds.  Measured on 4 x 256 queries over 16384 cached keys at 32/8 heads (288
+    // items): 322 -> 279 us per call with two chunks (dealing every unit's heaviest
+    // block first on top of that: no change).  The 0.6B varlen batch (984
+    // items for 512 slots) is left whole: split, it ran 59.5 -> 87 us.
+    const int kt = p.nw == 8 ? 128 : 64;
+    const int64_t max_tiles = ((int64_t)max_seqlen_k + kt - 1) / kt;
+    const int64_t n_real = ((int64_t)(total_q + bm - 1) / bm + num_seqs) * hkv * p.head_groups;
+    if (p.two_pass && n_real <= slots && max_tiles >= 2 * kSplitMinChunkTiles) {
+        const int nc = (int)std::min<int64_t>(4, slots / std::max<int64_t>(n_real, 1) + 1);
+        const size_t bytes = (size_t)p.n_work * nc * p.nw * kPartFloats * sizeof(float);
+        if (nc >= 2 && bytes <= kSplitMaxBytes) {
+            p.split_nc = nc;
+            p.split_bytes = bytes;
+        }
+    }
+    p.ok = true;
+    return p;
+}
+}  // namespace
+
+size_t prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               int32_t hq, int32_t hkv) {
+    const PrefillPlan p = plan_prefill(num_seqs, total_q, max_seqlen_q, max_seqlen_k, hq, hkv);
+    return p.ok && p.split_nc > 1 ? p.split_bytes : 0;
+}
+
+hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t stream) {
+    if (a.num_seqs == 0 || a.total_q == 0 || a.max_seqlen_q == 0) return hipSuccess;
+    const PrefillPlan p = plan_prefill(a.num_seqs, a.total_q, a.max_seqlen_q, a.max_seqlen_k, a.hq, a.hkv);
+    if (!p.ok) return hipErrorInvalidValue;
+    const int gw = p.gw, head_groups = p.head_groups, m_blocks = p.m_blocks, n_work = p.n_work, grid = p.grid;
+    const int grid_exact = p.grid_exact, n_iter = p.n_iter;
+    const int64_t chunk = p.chunk;
+    const bool wide = p.wide, two_pass = p.two_pass;
+    // The key split runs only with a workspace of the planned size (else the call
+    // runs unsplit, with the same results up to summation order).
+    const int nc = p.split_nc > 1 && a.workspace && a.workspace_bytes >= p.split_bytes &&
+                           (uintptr_t)a.workspace % 256 == 0
+                       ? p.split_nc
+                       : 1;
+    float* part = nc > 1 ? (float*)a.workspace : nullptr;
     // Each two-pass call gets a number of its own, so the exact pass can tell
     // whether this call's fast pass flagged anything (the device keeps the
     // highest number seen).  0 means exact pass only.
@@ -684,8 +844,11 @@ hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t stream) {
 #define PKV_PREFILL(GW_, PG_, NW_)                                                                               \
     do {                                                                                                         \
         if (two_pass)                                                                                            \
-            hipLaunchKernelGGL((prefill_kernel<GW_, PG_, NW_>), dim3(grid), dim3(64 * NW_), 0, stream, a,        \
-                               m_blocks, n_work, head_groups, (int32_t)chunk, call);                             \
+            hipLaunchKernelGGL((prefill_kernel<GW_, PG_, NW_>), dim3(grid * nc), dim3(64 * NW_), 0, stream, a,   \
+                               m_blocks, n_work, head_groups, (int32_t)chunk, call, nc, part);                   \
+        if (nc > 1)                                                                                              \
+            hipLaunchKernelGGL((prefill_merge_kernel<GW_, PG_, NW_>), dim3(n_work * NW_), dim3(64), 0, stream,   \
+                               a, m_blocks, n_work, head_groups, nc, part, call);                                \
         hipLaunchKernelGGL((prefill_exact_kernel<GW_, PG_, NW_>), dim3(grid_exact), dim3(64 * NW_), 0, stream,   \
                            a, m_blocks, n_work, head_groups, (int32_t)chunk, n_iter, call);                      \
     } while (0)

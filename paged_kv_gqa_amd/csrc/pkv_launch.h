@@ -63,8 +63,13 @@ struct PrefillArgs {
     const int32_t* block_table;  // NULL: contiguous K/V
     int32_t max_blocks;
     int64_t num_blocks;
+    void* workspace;             // key-split partial sums (NULL: no split)
+    size_t workspace_bytes;
 };
 hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t stream);
+// Workspace the call's key split uses (0: the call does not split).
+size_t prefill_workspace_bytes(int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               int32_t hq, int32_t hkv);
 
 struct DecodeArgs {
     const void* q;

@@ -82,7 +82,7 @@ def test_prefill_validation(lib):
     f = lib.pkv_attn_prefill_varlen
     o_fake = FAKE.value + (1 << 32)          # an output buffer away from q
     base = [FAKE, 4096, FAKE, 4096, FAKE, 4096, o_fake, FAKE, FAKE, 2, 337, 300, 300, 16, 8, 128, 0.088, 1, None, 0,
-            256, 0, None]
+            256, 0, None, 0, None]
     a = list(base); a[17] = 0                # causal = 0 is not built
     assert f(*a) == -2
     a = list(base); a[13] = 12               # Hq % Hkv
@@ -101,6 +101,25 @@ def test_prefill_validation(lib):
     assert f(*a) == -1 and "overlap" in _err(lib)
     a = list(base); a[9] = 0                 # no sequences: no-op
     assert f(*a) == 0
+    a = list(base); a[22] = ctypes.c_void_p(o_fake + (1 << 30) + 16); a[23] = 1 << 20   # misaligned workspace
+    assert f(*a) == -4 and "aligned" in _err(lib)
+    a = list(base); a[22] = ctypes.c_void_p(o_fake); a[23] = 1 << 20   # workspace on top of o
+    assert f(*a) == -4 and "overlap" in _err(lib)
+
+
+def test_prefill_workspace_query(lib):
+    """The key split is planned only for few query blocks over long keys, and the query
+    agrees with the binding's arguments (0 for invalid sizes)."""
+    ws = lib.pkv_attn_prefill_workspace_bytes
+    # 4 x 256 queries over 16384 keys at 32/8 heads: 128 blocks for 512 slots -> a split
+    n = ws(4, 1024, 256, 16384, 32, 8, 128)
+    assert n > 0 and n % 4 == 0 and n <= 512 << 20
+    assert ws(16, 32768, 2048, 4096, 32, 8, 128) == 0      # the 8B prefix batch: many blocks
+    assert ws(8, 7316, 1736, 1736, 16, 8, 128) == 0        # the 0.6B varlen batch
+    assert ws(4, 1024, 256, 512, 32, 8, 128) == 0          # short keys
+    assert ws(4, 1024, 256, 16384, 32, 8, 64) == 0         # head_dim
+    assert ws(4, 1024, 256, 16384, 12, 8, 128) == 0        # Hq % Hkv
+    assert ws(4, 1024, 300, 200, 32, 8, 128) == 0          # max_seqlen_q > max_seqlen_k
 
 
 def test_decode_validation_and_workspace(lib):
