@@ -10,7 +10,8 @@
 //
 // Design (HBM-bound: every K/V byte of the context is read once):
 //   * Split-K: a workgroup owns (sequence b, a group of 4 kv heads, split s)
-//     and covers up to 8 consecutive logical 256-token blocks.  Each of its 4
+//     and covers up to 8 consecutive logical 256-token blocks (down to 64 keys
+//     for short contexts at small batches).  Each of its 4
 //     waves owns one kv head and streams the whole split for it, so the waves
 //     read adjacent 256-byte pieces of every 2 KiB cache row (1 KiB per key
 //     and workgroup), each wave keeps its own online-softmax state and there
@@ -49,9 +50,12 @@ namespace {
 constexpr int kDecThreads = 256;
 // Tuning (measured on MI355X, Qwen3-8B and 0.6B decode workloads): splits of up
 // to 8 blocks, shortened one block at a time while the batch would have fewer
-// than ~1400 split items, a ring of 2 chunks of 16 keys per wave, 2 waves per
-// SIMD.  Longer splits amortise each workgroup's pipeline fill; deeper rings
-// did not pay.
+// than ~1400 split items, then halved to 8 and 4 chunks of 16 keys while the grid
+// fits the chip at once and no sequence gets more than 128 splits; a ring of 2 chunks of 16 keys per wave, 2
+// waves per SIMD.  Longer splits amortise each workgroup's pipeline fill; deeper
+// rings did not pay, not even at a batch of one, where a workgroup's time is its
+// chain of chunks (each chunk's V staging, scores, softmax and P V wait on one
+// another), which shorter splits cut instead.
 #ifndef PKV_DECODE_SPLIT
 #define PKV_DECODE_SPLIT 8
 #endif
@@ -70,6 +74,15 @@ constexpr float kLazyMax = 8.0f;   // log2 headroom of the lazy reference max
 constexpr int kDepth = PKV_DECODE_DEPTH;   // register ring: chunks in flight + the one computed
 constexpr int kCK = 16;                    // keys per wave per chunk (one 16-key MFMA tile)
 constexpr int kOcc = PKV_DECODE_OCC;       // waves per SIMD the register budget is sized for
+#ifndef PKV_DECODE_MIN_CHUNKS
+#define PKV_DECODE_MIN_CHUNKS 4
+#endif
+constexpr int kMinSplitChunks = PKV_DECODE_MIN_CHUNKS;   // shortest split (16-key chunks)
+#ifndef PKV_DECODE_MAX_SPLITS
+#define PKV_DECODE_MAX_SPLITS 128
+#endif
+constexpr int kMaxSplits = PKV_DECODE_MAX_SPLITS;        // splits per sequence the sub-block lengths allow
+constexpr int kResidentItems = 512;                      // split workgroups the chip holds at once (2 per CU)
 
 struct Workspace {
     float* part_o;   // [B][Hq][S][128]
@@ -96,19 +109,26 @@ struct Chunk {
 };
 }  // namespace
 
-int decode_split_blocks(int32_t num_seqs, int32_t hkv, int32_t max_blocks) {
-    int sb = kMaxSplitBlocks;
-    while (sb > 1) {
-        const int64_t items = (int64_t)num_seqs * ((hkv + 3) / 4) * ((max_blocks + sb - 1) / sb);
-        if (items >= kTargetItems) break;
-        --sb;
-    }
-    return sb;
+// Split length in 16-key chunks: whole blocks (8 down to 1) while the batch would
+// have fewer than kTargetItems split items; then halved (8, 4 chunks) while the
+// halved grid still fits the chip at once and no sequence gets more than
+// kMaxSplits splits for the merge to add -- short contexts at small batches, where
+// one workgroup's chain of chunks sets the time.
+int decode_split_chunks(int32_t num_seqs, int32_t hkv, int32_t max_blocks) {
+    constexpr int kCPB = kBlockSize / kCK;
+    const int64_t max_chunks = (int64_t)max_blocks * kCPB;
+    auto items = [&](int sc) { return (int64_t)num_seqs * ((hkv + 3) / 4) * ((max_chunks + sc - 1) / sc); };
+    int sc = kMaxSplitBlocks * kCPB;
+    while (sc > kCPB && items(sc) < kTargetItems) sc -= kCPB;
+    while (sc > kMinSplitChunks && items(sc) < kTargetItems && items(sc / 2) <= kResidentItems &&
+           (max_chunks + sc / 2 - 1) / (sc / 2) <= kMaxSplits)
+        sc /= 2;
+    return sc;
 }
 
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t max_blocks) {
-    const int sb = decode_split_blocks(num_seqs, hkv, max_blocks);
-    const int64_t ms = (max_blocks + sb - 1) / sb;
+    const int sc = decode_split_chunks(num_seqs, hkv, max_blocks);
+    const int64_t ms = ((int64_t)max_blocks * (kBlockSize / kCK) + sc - 1) / sc;
     const size_t o_bytes = align256((size_t)num_seqs * hq * ms * kHeadDim * sizeof(float));
     const size_t ml_bytes = align256((size_t)num_seqs * hq * ms * 2 * sizeof(float));
     const size_t work_bytes = align256((size_t)num_seqs * ms * sizeof(int32_t));
@@ -119,7 +139,7 @@ template <int G>
 __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ block_table, int32_t max_blocks,
-    int32_t hq, int32_t hkv, int64_t num_blocks, float scale_log2, int32_t split_blocks, int32_t max_splits,
+    int32_t hq, int32_t hkv, int64_t num_blocks, float scale_log2, int32_t split_chunks, int32_t max_splits,
     float* __restrict__ part_o, float* __restrict__ part_ml, const int32_t* __restrict__ work) {
     static_assert(G >= 1 && G <= 16, "GQA group must fit the 16 MFMA columns");
     // Dispatch order: split items by decreasing size (full splits first), so the
@@ -136,11 +156,15 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
     int ctx = context_lens[b];
     const int cap = max_blocks * kBlockSize;
     ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
-    const int nblk = (ctx + kBlockSize - 1) / kBlockSize;
-    const int blk0 = s * split_blocks;
-    if (blk0 >= nblk) return;
-    const int nb = min(split_blocks, nblk - blk0);   // blocks of this split
-    const int nchunks = nb * (kBlockSize / kCK);     // 16-key chunks of the split, all for this wave
+    // The split covers the context's 16-key chunks c0 .. c0 + nchunks - 1, all for
+    // this wave; they lie in blocks blk0 .. blk0 + nb - 1.
+    constexpr int kCPB = kBlockSize / kCK;           // chunks per block
+    const int nchk = (ctx + kCK - 1) / kCK;
+    const int c0 = s * split_chunks;
+    if (c0 >= nchk) return;
+    const int nchunks = min(split_chunks, nchk - c0);
+    const int blk0 = c0 / kCPB;
+    const int nb = (c0 + nchunks - 1) / kCPB - blk0 + 1;
 
     constexpr int kVPitch = kHeadDim * 2 + 32;       // bytes per V row in LDS (conflict-free transposed reads)
     __shared__ __attribute__((aligned(16))) unsigned char s_v[4][kCK * kVPitch];   // per-wave V tile
@@ -168,10 +192,11 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
         }
     }
 
-    // Chunk j covers keys 16*(j%16) .. +15 of block blk0 + j/16.
-    constexpr int kCPB = kBlockSize / kCK;           // chunks per block
-    auto block_of = [&](int j) { return __builtin_amdgcn_readlane(my_blk, j / kCPB); };
-    auto chunk_row0 = [&](int j) { return kCK * (j % kCPB); };
+    // Chunk j of the split is the context's chunk c0 + j: keys 16*((c0+j)%16) .. +15
+    // of block slot (c0+j)/16 - blk0.  Chunks j >= nchunks (the trip count's padding)
+    // are masked whole.
+    auto block_of = [&](int j) { return __builtin_amdgcn_readlane(my_blk, (c0 + j) / kCPB - blk0); };
+    auto chunk_row0 = [&](int j) { return kCK * ((c0 + j) % kCPB); };
     auto load = [&](Chunk& c, int j) {
         const int id = block_of(j);
         const int64_t phys = id < 0 ? 0 : id;
@@ -196,8 +221,8 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
     typedef __attribute__((address_space(3))) bf16x4* lds4_t;
 
     auto compute = [&](const Chunk& c, int j) {
-        const int key0 = (blk0 + j / kCPB) * kBlockSize + chunk_row0(j);
-        const int id = block_of(j);
+        const int key0 = (c0 + j) * kCK;
+        const int id = j < nchunks ? block_of(j) : -1;
         // ---- V rows into this wave's LDS tile; keys outside the context become zeros
 #pragma unroll
         for (int i = 0; i < kCK / 4; ++i) {
@@ -255,8 +280,8 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
     // chunk, an L2 hit), so the number of loads in flight is the same on every
     // path and each wait covers exactly the chunk about to be used.
     Chunk ring[kDepth];
-    // The trip count is padded to a multiple of the ring depth; padded chunks
-    // map to block slots >= nb whose id is -1, so all their keys are masked.
+    // The trip count is padded to a multiple of the ring depth; padded chunks are
+    // masked whole (their loads re-read the last chunk).
     const int ntrip = (nchunks + kDepth - 1) / kDepth * kDepth;
 #pragma unroll
     for (int u = 0; u < kDepth - 1; ++u) load(ring[u], min(u, nchunks - 1));
@@ -294,26 +319,26 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
 // share fall close together in time.  The order only schedules work: every
 // result is the same.
 __global__ void __launch_bounds__(1024) decode_order_kernel(const int32_t* __restrict__ context_lens,
-                                                            int32_t max_blocks, int32_t num_seqs, int32_t split_blocks,
+                                                            int32_t max_blocks, int32_t num_seqs, int32_t split_chunks,
                                                             int32_t max_splits, int32_t* __restrict__ work) {
-    __shared__ int32_t s_bin[kMaxSplitBlocks + 1];
+    __shared__ int32_t s_bin[kMaxSplitBlocks * (kBlockSize / kCK) + 1];
     const int tid = threadIdx.x;
     const int cap = max_blocks * kBlockSize;
     const int n_items = num_seqs * max_splits;
-    auto key = [&](int it) {   // split_blocks - (blocks of the item): 0 = full
+    auto key = [&](int it) {   // split_chunks - (chunks of the item): 0 = full
         const int b = it / max_splits, s = it - b * max_splits;
         int ctx = context_lens[b];
         ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
-        const int nb = (ctx + kBlockSize - 1) / kBlockSize - s * split_blocks;
-        return split_blocks - (nb < 0 ? 0 : (nb > split_blocks ? split_blocks : nb));
+        const int nc = (ctx + kCK - 1) / kCK - s * split_chunks;
+        return split_chunks - (nc < 0 ? 0 : (nc > split_chunks ? split_chunks : nc));
     };
-    if (tid <= split_blocks) s_bin[tid] = 0;
+    if (tid <= split_chunks) s_bin[tid] = 0;
     __syncthreads();
     for (int it = tid; it < n_items; it += 1024) atomicAdd(&s_bin[key(it)], 1);
     __syncthreads();
     if (tid == 0) {   // exclusive prefix over the bins
         int run = 0;
-        for (int i = 0; i <= split_blocks; ++i) {
+        for (int i = 0; i <= split_chunks; ++i) {
             const int c = s_bin[i];
             s_bin[i] = run;
             run += c;
@@ -332,8 +357,12 @@ __global__ void __launch_bounds__(1024) decode_order_kernel(const int32_t* __res
 // with uniform addresses (every lane the same split), the partial outputs as
 // 512 contiguous bytes per split, four splits' loads in flight at a time.
 constexpr int kCombineWaves = 4;
+#ifndef PKV_COMBINE_IN_FLIGHT
+#define PKV_COMBINE_IN_FLIGHT 4
+#endif
+constexpr int kCombineInFlight = PKV_COMBINE_IN_FLIGHT;   // splits whose loads are in flight together
 __global__ void __launch_bounds__(64 * kCombineWaves) decode_combine_kernel(
-    const int32_t* __restrict__ context_lens, int32_t max_blocks, int32_t hq, int32_t split_blocks,
+    const int32_t* __restrict__ context_lens, int32_t max_blocks, int32_t hq, int32_t split_chunks,
     int32_t max_splits, const float* __restrict__ part_o, const float* __restrict__ part_ml,
     uint16_t* __restrict__ o) {
     const int lane = threadIdx.x & 63;
@@ -342,8 +371,7 @@ __global__ void __launch_bounds__(64 * kCombineWaves) decode_combine_kernel(
     int ctx = context_lens[b];
     const int cap = max_blocks * kBlockSize;
     ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
-    const int nblk = (ctx + kBlockSize - 1) / kBlockSize;
-    const int ns = (nblk + split_blocks - 1) / split_blocks;
+    const int ns = ((ctx + kCK - 1) / kCK + split_chunks - 1) / split_chunks;
     const int64_t bh = (int64_t)b * hq + h;
     const float* ml = part_ml + bh * max_splits * 2;
     const float* po = part_o + bh * max_splits * kHeadDim + 2 * lane;
@@ -356,17 +384,17 @@ __global__ void __launch_bounds__(64 * kCombineWaves) decode_combine_kernel(
     float L = 0.f;
     float acc0 = 0.f, acc1 = 0.f;
     int s = 0;
-    for (; s + 4 <= ns; s += 4) {
-        float2 p[4];
-        float m[4], l[4];
+    for (; s + kCombineInFlight <= ns; s += kCombineInFlight) {
+        float2 p[kCombineInFlight];
+        float m[kCombineInFlight], l[kCombineInFlight];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kCombineInFlight; ++i) {
             p[i] = *reinterpret_cast<const float2*>(po + (int64_t)(s + i) * kHeadDim);
             m[i] = ml[2 * (s + i)];
             l[i] = ml[2 * (s + i) + 1];
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kCombineInFlight; ++i) {
             const float w = exp2f(m[i] - ref);
             L = fmaf(l[i], w, L);
             acc0 = fmaf(p[i].x, w, acc0);
@@ -422,23 +450,23 @@ hipError_t decode_scratch(void** ptr) {
 hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t stream) {
     if (a.num_seqs == 0) return hipSuccess;
     const int G = a.hq / a.hkv;
-    const int sb = decode_split_blocks(a.num_seqs, a.hkv, a.max_blocks);
-    const int ms = (a.max_blocks + sb - 1) / sb;
+    const int sc = decode_split_chunks(a.num_seqs, a.hkv, a.max_blocks);
+    const int ms = (a.max_blocks * (kBlockSize / kCK) + sc - 1) / sc;
     Workspace w = carve(a.workspace, a.num_seqs, a.hq, ms);
     dim3 grid((a.hkv + 3) / 4, a.num_seqs, ms);
     // The size-ordered dispatch pays when workgroups queue for the chip; when the
     // whole grid fits at once (two split workgroups per CU, 256 CUs) the order kernel
     // is skipped: one launch less on short, small-batch steps.
-    const bool ordered = (int64_t)grid.x * grid.y * grid.z > 512;
+    const bool ordered = (int64_t)grid.x * grid.y * grid.z > kResidentItems;
     if (ordered)
         hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(1024), 0, stream, a.context_lens, a.max_blocks,
-                           a.num_seqs, sb, ms, w.work);
+                           a.num_seqs, sc, ms, w.work);
     const int32_t* work = ordered ? w.work : nullptr;
 #define PKV_DECODE_CASE(GG)                                                                                       \
     case GG:                                                                                                      \
         hipLaunchKernelGGL(decode_split_kernel<GG>, grid, dim3(kDecThreads), 0, stream, (const uint16_t*)a.q,     \
                            (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.context_lens, a.block_table, \
-                           a.max_blocks, a.hq, a.hkv, a.num_blocks, a.scale_log2, sb, ms, w.part_o, w.part_ml,   \
+                           a.max_blocks, a.hq, a.hkv, a.num_blocks, a.scale_log2, sc, ms, w.part_o, w.part_ml,   \
                            work);                                                                                 \
         break;
     switch (G) {
@@ -455,7 +483,7 @@ hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_combine_kernel, dim3((a.hq + kCombineWaves - 1) / kCombineWaves, a.num_seqs),
                        dim3(64 * kCombineWaves), 0, stream, a.context_lens,
-                       a.max_blocks, a.hq, sb, ms, w.part_o, w.part_ml, (uint16_t*)a.o);
+                       a.max_blocks, a.hq, sc, ms, w.part_o, w.part_ml, (uint16_t*)a.o);
     return hipGetLastError();
 }
 

@@ -88,7 +88,7 @@ struct DecodeArgs {
 };
 // Number of 256-token blocks one split-K work item covers, and the number of
 // splits per sequence the workspace is sized for.
-int decode_split_blocks(int32_t num_seqs, int32_t hkv, int32_t max_blocks);
+int decode_split_chunks(int32_t num_seqs, int32_t hkv, int32_t max_blocks);
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t max_blocks);
 hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t stream);
 // Size of the fixed device array pkv_attn_decode_paged_noalloc uses as its workspace.

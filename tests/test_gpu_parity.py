@@ -634,6 +634,25 @@ def test_decode_small_ragged(dev, hq, hkv):
     assert torch.equal(r["o"], r["o_perm"]), "physical block placement changed the output"
 
 
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (16, 8), (8, 1)])
+def test_decode_short_contexts_sub_block_splits(dev, hq, hkv):
+    """Short contexts at a small batch run in splits of 64 keys (4 chunks of 16 keys),
+    not whole blocks: splits that end mid-block, partial chunks, padded ring trips,
+    empty splits past the context.  NaN canaries and a permuted pool as above."""
+    ctx = [1, 15, 16, 17, 63, 64, 65, 130, 700, 0]
+    mb = max(-(-c // 256) for c in ctx) + 1
+    # the workspace shows the split length: 16 splits of 64 keys per 4-block row
+    need = pkv.decode_workspace_bytes(len(ctx), hq, hkv, mb)
+    assert need >= len(ctx) * hq * (mb * 256 // 64) * D * 4, "expected 64-key splits"
+    _say(f"decode short contexts {ctx}, {hq}/{hkv} heads, 64-key splits")
+    r = _decode_case(dev, ctx, hq, hkv, seed=hq + 2, nan_canaries=True, permute=True)
+    got = f64(r["o"])
+    check_attn(got[:-1], r["ref"][:-1], "decode sub-block splits")
+    assert np.all(got[-1] == 0.0), "zero-length context must give a zero row"
+    assert torch.equal(r["o"], r["o_nan"]), "bytes outside the context changed the output"
+    assert torch.equal(r["o"], r["o_perm"]), "physical block placement changed the output"
+
+
 def test_decode_long_context_many_splits(dev):
     ctx = [32768, 20000, 9000]
     _say(f"decode long contexts {ctx}")
