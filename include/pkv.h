@@ -359,7 +359,13 @@ PKV_API int pkv_sample_gumbel(const void* logits, int64_t logits_row_stride, int
  *     pkv_qk_norm_rope_store(q, k, v columns of qkv rows 0..batch-1 -> q_out,
  *                            k_cache / v_cache at slot_mapping)
  *     pkv_attn_decode_paged(q_out -> o, context_lens, block_table)
- * on the buffers the descriptor names.  Those buffers are owned by the caller,
+ * on the buffers the descriptor names, with the same checks and, bit for bit,
+ * the same results, run as two kernels: the decode split kernel applies
+ * QK-Norm + RoPE to the rows it attends with and stores each row's new k' / v,
+ * then the merge.  The equality needs what the engine's metadata gives: each
+ * row's slot is the cache row of its key context_lens[b] - 1 (or -1 for a
+ * padded row).  Otherwise the slot is still written, but the row's attention
+ * reads whatever that key's cache row holds.  Those buffers are owned by the caller,
  * sized for max_batch rows, and must stay allocated and at the same addresses
  * while a graph built from the descriptor exists (a graph bakes them in): a
  * caller writes each step's inputs into them, then launches.

@@ -112,18 +112,18 @@ int pkv_qk_norm_rope(const void* q, int64_t q_row_stride, const void* k, int64_t
                     fn);
 }
 
-int pkv_qk_norm_rope_store(const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride,
-                           const void* v, int64_t v_row_stride, void* q_out, void* k_out, void* k_cache,
-                           void* v_cache, int64_t num_slots, const int32_t* slot_mapping, const int64_t* positions,
-                           int32_t n_tokens, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                           const void* q_norm_weight, const void* k_norm_weight, float eps,
-                           const float* cos_sin_cache, int32_t max_position, void* stream) {
-    const char* fn = "pkv_qk_norm_rope_store";
+namespace {
+// Checks of pkv_qk_norm_rope_store (also run by the decode step, which fuses it).
+int norm_store_check(const char* fn, const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride,
+                     const void* v, int64_t v_row_stride, void* q_out, void* k_out, void* k_cache, void* v_cache,
+                     int64_t num_slots, const int32_t* slot_mapping, const int64_t* positions, int32_t n_tokens,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, const void* q_norm_weight,
+                     const void* k_norm_weight, float eps, const float* cos_sin_cache, int32_t max_position) {
     int rc = check_heads(fn, num_q_heads, num_kv_heads, head_dim);
     if (rc) return rc;
     PKV_REQUIRE(n_tokens >= 0, PKV_ERR_INVALID_ARG, "%s: n_tokens must be >= 0 (got %d)", fn, n_tokens);
     PKV_REQUIRE(num_slots >= 0, PKV_ERR_INVALID_ARG, "%s: num_slots must be >= 0", fn);
-    if (n_tokens == 0) return ok();
+    if (n_tokens == 0) return PKV_OK;
     PKV_REQUIRE(q && k && v && q_out && k_cache && v_cache && slot_mapping && positions && q_norm_weight &&
                     k_norm_weight && cos_sin_cache,
                 PKV_ERR_INVALID_ARG, "%s: a required pointer is NULL (only k_out may be NULL)", fn);
@@ -146,6 +146,22 @@ int pkv_qk_norm_rope_store(const void* q, int64_t q_row_stride, const void* k, i
                 "%s: in-place q needs q_row_stride == num_q_heads*head_dim", fn);
     PKV_REQUIRE(!k_out || k_out != k || k_row_stride == kw, PKV_ERR_INVALID_ARG,
                 "%s: in-place k needs k_row_stride == num_kv_heads*head_dim", fn);
+    return PKV_OK;
+}
+}  // namespace
+
+int pkv_qk_norm_rope_store(const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride,
+                           const void* v, int64_t v_row_stride, void* q_out, void* k_out, void* k_cache,
+                           void* v_cache, int64_t num_slots, const int32_t* slot_mapping, const int64_t* positions,
+                           int32_t n_tokens, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           const void* q_norm_weight, const void* k_norm_weight, float eps,
+                           const float* cos_sin_cache, int32_t max_position, void* stream) {
+    const char* fn = "pkv_qk_norm_rope_store";
+    const int rc = norm_store_check(fn, q, q_row_stride, k, k_row_stride, v, v_row_stride, q_out, k_out, k_cache,
+                                    v_cache, num_slots, slot_mapping, positions, n_tokens, num_q_heads, num_kv_heads,
+                                    head_dim, q_norm_weight, k_norm_weight, eps, cos_sin_cache, max_position);
+    if (rc) return rc;
+    if (n_tokens == 0) return ok();
     return launched(pkv::launch_qk_norm_rope_store(q, q_row_stride, k, k_row_stride, v, v_row_stride, q_out, k_out,
                                                    k_cache, v_cache, num_slots, slot_mapping, positions, n_tokens,
                                                    num_q_heads, num_kv_heads, q_norm_weight, k_norm_weight, eps,
@@ -339,6 +355,55 @@ int pkv_attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
     a.workspace = workspace;
     return launched(pkv::launch_attn_decode(a, (hipStream_t)stream), fn);
 }
+
+extern "C++" {
+namespace pkv {
+// One decode step (pkv_decode_step and its graphs): the checks of
+// pkv_qk_norm_rope_store and pkv_attn_decode_paged on the step's buffers, then one
+// split kernel that also applies QK-Norm + RoPE to the step's q rows and stores its
+// k' / v rows, and the merge.  The results are those of calling the two entry
+// points in turn, bit for bit, when each row's slot is its key ctx - 1 (as the
+// engine's slot mapping has it); a slot elsewhere is still written, but that
+// row's attention then reads whatever its cache row holds.
+int decode_step_run(const pkv_decode_step_desc& d, int32_t batch, hipStream_t stream) {
+    const int64_t k0 = (int64_t)d.num_q_heads * d.head_dim, v0 = k0 + (int64_t)d.num_kv_heads * d.head_dim;
+    const uint16_t* qkv = (const uint16_t*)d.qkv;
+    int rc = norm_store_check("pkv_decode_step", qkv, d.qkv_row_stride, qkv + k0, d.qkv_row_stride, qkv + v0,
+                              d.qkv_row_stride, d.q_out, nullptr, d.k_cache, d.v_cache, d.num_blocks * d.block_size,
+                              d.slot_mapping, d.positions, batch, d.num_q_heads, d.num_kv_heads, d.head_dim,
+                              d.q_norm_weight, d.k_norm_weight, d.eps, d.cos_sin_cache, d.max_position);
+    if (rc) return rc;
+    pkv::DecodeArgs a;
+    rc = decode_args("pkv_decode_step", d.q_out, d.k_cache, d.v_cache, d.o, d.context_lens, d.block_table,
+                     d.max_blocks_per_seq, batch, d.num_q_heads, d.num_kv_heads, d.head_dim, d.block_size,
+                     d.num_blocks, d.softmax_scale, a);
+    if (rc) return rc;
+    if (batch == 0) return ok();
+    const size_t need = pkv_attn_decode_workspace_bytes(batch, d.num_q_heads, d.num_kv_heads, d.head_dim,
+                                                        d.max_blocks_per_seq, d.block_size);
+    PKV_REQUIRE(d.workspace != nullptr && d.workspace_bytes >= need, PKV_ERR_WORKSPACE,
+                "pkv_decode_step: workspace of %zu bytes needed, %zu given", need,
+                d.workspace ? d.workspace_bytes : (size_t)0);
+    PKV_REQUIRE((uintptr_t)d.workspace % 256 == 0, PKV_ERR_WORKSPACE, "pkv_decode_step: workspace must be 256-byte aligned");
+    a.workspace = d.workspace;
+    pkv::StepArgs sa;
+    sa.qkv = qkv;
+    sa.qkv_stride = d.qkv_row_stride;
+    sa.positions = d.positions;
+    sa.slot_mapping = d.slot_mapping;
+    sa.q_norm_weight = (const uint16_t*)d.q_norm_weight;
+    sa.k_norm_weight = (const uint16_t*)d.k_norm_weight;
+    sa.eps = d.eps;
+    sa.table = d.cos_sin_cache;
+    sa.max_pos = d.max_position;
+    sa.q_out = (uint16_t*)d.q_out;
+    sa.k_cache = (uint16_t*)d.k_cache;
+    sa.v_cache = (uint16_t*)d.v_cache;
+    sa.num_slots = d.num_blocks * d.block_size;
+    return launched(pkv::launch_decode_step(a, sa, stream), "pkv_decode_step");
+}
+}  // namespace pkv
+}  // extern "C++"
 
 int pkv_attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o,
                                   const int32_t* context_lens, const int32_t* block_table,

@@ -135,12 +135,86 @@ size_t decode_workspace_bytes(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t
     return o_bytes + ml_bytes + work_bytes;
 }
 
-template <int G>
+// QK-Norm + RoPE of one 128-element head vector held by the four lanes of a
+// column (lanes col + 16 grp, grp = 0..3) in the decode split kernel's operand
+// layout: x[st] holds dims 8 grp + 32 st .. +7, so the rotation partner of piece
+// st (dims +-64) is piece st ^ 2 of the same lane.  The arithmetic is that of the
+// standalone QK-Norm + RoPE kernel (rope.hip, norm_rope_apply), in the same order:
+// the per-piece sums of squares are combined along the same tree as its 16-lane
+// butterfly (its lane grp + 4 st; partners xor 8, 4, 2, 1 are here pieces st ^ 2,
+// st ^ 1 and lanes xor 32, xor 16), so the results are bit-identical.
+__device__ __forceinline__ void norm_rope_cols(const u32x4 (&x)[4], const uint16_t* __restrict__ gamma,
+                                               const float* __restrict__ trow, float eps, int grp, u32x4 (&out)[4]) {
+    float xa[4][8];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            xa[st][2 * w] = bf16lo(x[st][w]);
+            xa[st][2 * w + 1] = bf16hi(x[st][w]);
+        }
+    float ssp[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += xa[st][e] * xa[st][e];
+        ssp[st] = ss;
+    }
+    float t[4], u[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) t[st] = ssp[st] + ssp[st ^ 2];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) u[st] = t[st] + t[st ^ 1];
+    float ss = u[0];
+    ss += __shfl_xor(ss, 32, 64);
+    ss += __shfl_xor(ss, 16, 64);
+    const float r = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const float* cs = trow + 8 * grp + 32 * (st & 1);
+        const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs);
+        const f32x4 c1 = *reinterpret_cast<const f32x4*>(cs + 4);
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(cs + 64);
+        const f32x4 s1 = *reinterpret_cast<const f32x4*>(cs + 68);
+        float cv[8], sv[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            cv[i] = c0[i];
+            cv[4 + i] = c1[i];
+            sv[i] = s0[i];
+            sv[4 + i] = s1[i];
+        }
+        const u32x4 go = ldg128(gamma + 8 * grp + 32 * st);
+        const u32x4 gp = ldg128(gamma + 8 * grp + 32 * (st ^ 2));
+        // The sign as a register value, as in the standalone kernel (where it depends
+        // on the lane): a constant here would let the compiler fold it and fuse the
+        // other product into the add, which rounds differently.
+        float sgn;
+        asm("v_mov_b32 %0, %1" : "=v"(sgn) : "v"(st < 2 ? -1.0f : 1.0f));
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            float o2[2];
+#pragma unroll
+            for (int hlf = 0; hlf < 2; ++hlf) {
+                const int e = 2 * w + hlf;
+                const float ga = hlf ? bf16hi(go[w]) : bf16lo(go[w]);
+                const float gb = hlf ? bf16hi(gp[w]) : bf16lo(gp[w]);
+                const float ya = xa[st][e] * r * ga;
+                const float yb = xa[st ^ 2][e] * r * gb;
+                o2[hlf] = ya * cv[e] + sgn * (yb * sv[e]);
+            }
+            out[st][w] = pack_bf16x2(o2[0], o2[1]);
+        }
+    }
+}
+
+template <int G, bool kStep>
 __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ block_table, int32_t max_blocks,
     int32_t hq, int32_t hkv, int64_t num_blocks, float scale_log2, int32_t split_chunks, int32_t max_splits,
-    float* __restrict__ part_o, float* __restrict__ part_ml, const int32_t* __restrict__ work) {
+    float* __restrict__ part_o, float* __restrict__ part_ml, const int32_t* __restrict__ work, StepArgs sa) {
     static_assert(G >= 1 && G <= 16, "GQA group must fit the 16 MFMA columns");
     // Dispatch order: split items by decreasing size (full splits first), so the
     // smallest pieces of work come last and the tail stays short.  Without an
@@ -161,10 +235,12 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
     constexpr int kCPB = kBlockSize / kCK;           // chunks per block
     const int nchk = (ctx + kCK - 1) / kCK;
     const int c0 = s * split_chunks;
-    if (c0 >= nchk) return;
-    const int nchunks = min(split_chunks, nchk - c0);
+    // In a step, split 0 of every row also writes the row's q' (and, with an empty
+    // context, stores the new token), so it runs even when it has no keys.
+    if (c0 >= nchk && !(kStep && s == 0)) return;
+    const int nchunks = c0 < nchk ? min(split_chunks, nchk - c0) : 0;
     const int blk0 = c0 / kCPB;
-    const int nb = (c0 + nchunks - 1) / kCPB - blk0 + 1;
+    const int nb = nchunks > 0 ? (c0 + nchunks - 1) / kCPB - blk0 + 1 : 0;
 
     constexpr int kVPitch = kHeadDim * 2 + 32;       // bytes per V row in LDS (conflict-free transposed reads)
     __shared__ __attribute__((aligned(16))) unsigned char s_v[4][kCK * kVPitch];   // per-wave V tile
@@ -182,7 +258,58 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
     const int col = lane & 15, grp = lane >> 4;
     // B operand of the scores: q of head g*G + col, dims 8*grp + 32*st .. +7, zero for col >= G.
     bf16x8 qb[4];
-    {
+    // Step: the new token's k' (pieces as q's, for lanes col == its chunk row) and v
+    // (this lane's 8 dims), patched into the chunk that holds key ctx - 1.
+    u32x4 kn[4], vn = {0u, 0u, 0u, 0u};
+    bool inject = false;
+    if (kStep) {
+        const bool on = col < G;
+        const uint16_t* row_in = sa.qkv + (int64_t)b * sa.qkv_stride;
+        int64_t pos = sa.positions[b];
+        pos = pos < 0 ? 0 : (pos >= sa.max_pos ? (int64_t)sa.max_pos - 1 : pos);
+        const float* trow = sa.table + pos * kHeadDim;
+        u32x4 x[4], qn[4];
+        const uint16_t* qr = row_in + ((int64_t)g * G + (on ? col : 0)) * kHeadDim + 8 * grp;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) x[st] = ldg128(qr + 32 * st);
+        norm_rope_cols(x, sa.q_norm_weight, trow, sa.eps, grp, qn);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) qb[st] = __builtin_bit_cast(bf16x8, on ? qn[st] : u32x4{0u, 0u, 0u, 0u});
+        if (s == 0 && on) {
+            uint16_t* qo = sa.q_out + ((int64_t)b * hq + (int64_t)g * G + col) * kHeadDim + 8 * grp;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) stg128(qo + 32 * st, qn[st]);
+        }
+        // The split holding the context's last chunk (split 0 when the context is
+        // empty) owns the new token: k' and v to its cache slot, and into its chunk.
+        if ((nchunks > 0 && c0 + nchunks == nchk) || (nchk == 0 && s == 0)) {
+            const uint16_t* kr = row_in + ((int64_t)hq + g) * kHeadDim + 8 * grp;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) x[st] = ldg128(kr + 32 * st);
+            norm_rope_cols(x, sa.k_norm_weight, trow, sa.eps, grp, kn);
+            vn = ldg128(row_in + ((int64_t)hq + hkv + g) * kHeadDim + 8 * col);
+            const int64_t slot = sa.slot_mapping[b];
+            if (slot >= 0 && slot < sa.num_slots) {
+                const int64_t rowel = (int64_t)hkv * kHeadDim;
+                if (col == 0) {
+#pragma unroll
+                    for (int st = 0; st < 4; ++st)
+                        stg128(sa.k_cache + slot * rowel + (int64_t)g * kHeadDim + 8 * grp + 32 * st, kn[st]);
+                }
+                if (grp == 0) stg128(sa.v_cache + slot * rowel + (int64_t)g * kHeadDim + 8 * col, vn);
+                // key ctx - 1 is that slot's row (the engine writes each new token at
+                // the end of its context): take it from registers, not from memory
+                // this step is writing
+                if (nchunks > 0) {
+                    const int kl = ctx - 1;
+                    const int32_t id = block_table[(int64_t)b * max_blocks + kl / kBlockSize];
+                    inject = id >= 0 && (int64_t)id < num_blocks &&
+                             (int64_t)id * kBlockSize + kl % kBlockSize == slot;
+                }
+            }
+        }
+        if (nchunks == 0) return;
+    } else {
         const bool on = col < G;
         const uint16_t* qr = q + ((int64_t)b * hq + (int64_t)g * G + (on ? col : 0)) * kHeadDim + 8 * grp;
 #pragma unroll
@@ -291,6 +418,18 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
             const int j = j0 + u;
             load(ring[(u + kDepth - 1) % kDepth], min(j + kDepth - 1, nchunks - 1));
             __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of this chunk's math
+            if (kStep && inject && j == nchunks - 1) {
+                // the new token is row (ctx - 1) % 16 of this chunk: K is the A operand
+                // (key = lane % 16), V rows are key grp + 4 i
+                const int rr = (ctx - 1) % kCK;
+                if (col == rr) {
+#pragma unroll
+                    for (int st = 0; st < 4; ++st) ring[u].k[st] = kn[st];
+                }
+#pragma unroll
+                for (int i = 0; i < kCK / 4; ++i)
+                    if (grp == rr % 4 && i == rr / 4) ring[u].v[i] = vn;
+            }
             compute(ring[u], j);
         }
     }
@@ -447,7 +586,9 @@ hipError_t decode_scratch(void** ptr) {
     return hipSuccess;
 }
 
-hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t stream) {
+namespace {
+template <bool kStep>
+hipError_t launch_decode_impl(const DecodeArgs& a, const StepArgs& sa, hipStream_t stream) {
     if (a.num_seqs == 0) return hipSuccess;
     const int G = a.hq / a.hkv;
     const int sc = decode_split_chunks(a.num_seqs, a.hkv, a.max_blocks);
@@ -464,10 +605,10 @@ hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t stream) {
     const int32_t* work = ordered ? w.work : nullptr;
 #define PKV_DECODE_CASE(GG)                                                                                       \
     case GG:                                                                                                      \
-        hipLaunchKernelGGL(decode_split_kernel<GG>, grid, dim3(kDecThreads), 0, stream, (const uint16_t*)a.q,     \
-                           (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.context_lens, a.block_table, \
-                           a.max_blocks, a.hq, a.hkv, a.num_blocks, a.scale_log2, sc, ms, w.part_o, w.part_ml,   \
-                           work);                                                                                 \
+        hipLaunchKernelGGL((decode_split_kernel<GG, kStep>), grid, dim3(kDecThreads), 0, stream,                  \
+                           (const uint16_t*)a.q, (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache,          \
+                           a.context_lens, a.block_table, a.max_blocks, a.hq, a.hkv, a.num_blocks, a.scale_log2, \
+                           sc, ms, w.part_o, w.part_ml, work, sa);                                                \
         break;
     switch (G) {
         PKV_DECODE_CASE(1)
@@ -485,6 +626,15 @@ hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t stream) {
                        dim3(64 * kCombineWaves), 0, stream, a.context_lens,
                        a.max_blocks, a.hq, sc, ms, w.part_o, w.part_ml, (uint16_t*)a.o);
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t stream) {
+    return launch_decode_impl<false>(a, StepArgs{}, stream);
+}
+
+hipError_t launch_decode_step(const DecodeArgs& a, const StepArgs& st, hipStream_t stream) {
+    return launch_decode_impl<true>(a, st, stream);
 }
 
 }  // namespace pkv

@@ -10,7 +10,8 @@
 // them; their context length is 0, so decode reads no key for them.
 //
 // One step = pkv_qk_norm_rope_store over the step's qkv rows (q', and k' / v
-// into their cache slots) followed by pkv_attn_decode_paged.  The graph for
+// into their cache slots) followed by pkv_attn_decode_paged, run as one split
+// kernel that does both (decode_step_run) and the merge.  The graph for
 // bucket n is exactly the eager step at batch n, captured once; a replay for
 // a batch b < n first marks rows [b, n) as padding with one small kernel,
 // unless the caller keeps those rows padded itself (PKV_DECODE_CALLER_PADS),
@@ -36,18 +37,7 @@ __global__ void __launch_bounds__(256) pad_rows_kernel(int32_t* __restrict__ slo
 }
 
 int step(const pkv_decode_step_desc& d, int32_t batch, hipStream_t stream) {
-    const int64_t q0 = 0, k0 = (int64_t)d.num_q_heads * d.head_dim, v0 = k0 + (int64_t)d.num_kv_heads * d.head_dim;
-    const uint16_t* qkv = (const uint16_t*)d.qkv;
-    int rc = pkv_qk_norm_rope_store(qkv + q0, d.qkv_row_stride, qkv + k0, d.qkv_row_stride, qkv + v0,
-                                    d.qkv_row_stride, d.q_out, nullptr, d.k_cache, d.v_cache,
-                                    d.num_blocks * d.block_size, d.slot_mapping, d.positions, batch, d.num_q_heads,
-                                    d.num_kv_heads, d.head_dim, d.q_norm_weight, d.k_norm_weight, d.eps,
-                                    d.cos_sin_cache, d.max_position, stream);
-    if (rc) return rc;  // the message is already set
-    rc = pkv_attn_decode_paged(d.q_out, d.k_cache, d.v_cache, d.o, d.context_lens, d.block_table,
-                               d.max_blocks_per_seq, batch, d.num_q_heads, d.num_kv_heads, d.head_dim, d.block_size,
-                               d.num_blocks, d.softmax_scale, d.workspace, d.workspace_bytes, stream);
-    return rc;
+    return pkv::decode_step_run(d, batch, stream);
 }
 
 int check_desc(const pkv_decode_step_desc* d) {

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pkv.h"
+
 namespace pkv {
 
 // Sets the thread-local message pkv_last_error() returns; returns code.
@@ -86,11 +88,34 @@ struct DecodeArgs {
     float scale_log2;
     void* workspace;
 };
-// Number of 256-token blocks one split-K work item covers, and the number of
-// splits per sequence the workspace is sized for.
+// The decode step's own inputs when QK-Norm + RoPE + scatter run inside the
+// split kernel (launch_decode_step): the step's raw q | k | v rows, their
+// positions and cache slots, the norm weights and the RoPE table.
+struct StepArgs {
+    const uint16_t* qkv;         // bf16 rows: q (hq heads) | k (hkv) | v (hkv)
+    int64_t qkv_stride;          // elements
+    const int64_t* positions;
+    const int32_t* slot_mapping;
+    const uint16_t* q_norm_weight;
+    const uint16_t* k_norm_weight;
+    float eps;
+    const float* table;          // fp32 [max_pos][128]: cos half, sin half
+    int32_t max_pos;
+    uint16_t* q_out;             // q' of the step
+    uint16_t* k_cache;           // the caches, written at the new tokens' slots
+    uint16_t* v_cache;
+    int64_t num_slots;
+};
+// Length of one split-K work item in 16-key chunks.
 int decode_split_chunks(int32_t num_seqs, int32_t hkv, int32_t max_blocks);
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t max_blocks);
 hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t stream);
+// One decode step: q' and the new tokens' k' / v computed inside the split kernel
+// (a.q unused), then the same merge as launch_attn_decode.
+hipError_t launch_decode_step(const DecodeArgs& a, const StepArgs& st, hipStream_t stream);
+// The checked decode step (pkv_decode_step and the graph captures): status code,
+// message set on failure.
+int decode_step_run(const pkv_decode_step_desc& d, int32_t batch, hipStream_t stream);
 // Size of the fixed device array pkv_attn_decode_paged_noalloc uses as its workspace.
 constexpr size_t kDecodeScratchBytes = size_t(96) << 20;
 // Its device address on the current device (looked up once per device).

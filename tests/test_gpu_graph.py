@@ -157,3 +157,59 @@ def test_decode_graph_batch_above_largest_bucket_is_refused(dev):
     torch.cuda.synchronize()
     assert st.o[:4].float().abs().max().item() == 0.0        # every row has context 0
     st.close()
+
+
+@pytest.mark.parametrize("hq,hkv,batch,max_ctx", [
+    (32, 8, 5, 1000),     # short contexts, small batch: 64-key splits
+    (16, 8, 9, 3000),     # G = 2
+    (8, 8, 3, 700),       # G = 1
+    (64, 8, 2, 600),      # G = 8
+    (32, 8, 300, 2100),   # a grid past the chip: size-ordered dispatch
+])
+def test_decode_step_equals_the_two_calls(dev, hq, hkv, batch, max_ctx):
+    """The step runs QK-Norm + RoPE + scatter inside the decode split kernel; its q',
+    caches and output must equal, byte for byte, QK-Norm + RoPE + scatter followed by
+    the decode call on the same inputs.  The batch holds a padded row (slot -1,
+    context 0), a row with an empty context whose token is still stored, and contexts
+    whose last key falls on every row of a 16-key chunk."""
+    shape = wl.QWEN3_8B if hq == 32 else wl.QWEN3_0_6B
+    width = (hq + 2 * hkv) * D
+    _say(f"decode step vs two calls: {hq}/{hkv} heads, batch {batch}, contexts < {max_ctx}")
+    rng = wl.rng_for(96, hq + batch, 0)
+    mb = -(-max_ctx // 256)
+    nb = batch * mb + 2
+    perm = rng.permutation(nb)[:batch * mb]
+    bt = perm.reshape(batch, mb).astype(np.int32)
+    ctx = rng.integers(1, max_ctx, size=batch).astype(np.int64)
+    ctx[:min(batch, 16)] = 17 * np.arange(min(batch, 16)) + 1   # key ctx - 1 on row i of its 16-key chunk
+    ctx = np.minimum(ctx, max_ctx - 1)
+    pos = ctx - 1
+    slots = np.array([bt[i, pos[i] // 256] * 256 + pos[i] % 256 for i in range(batch)], np.int32)
+    ctx32 = ctx.astype(np.int32)
+    slots[batch - 1], ctx32[batch - 1] = -1, 0            # a padded row
+    if batch > 2:
+        ctx32[batch - 2] = 0                               # no context, the token is still stored
+    qkv = wl.normal_bf16(rng, (batch, width))
+    pool = wl.normal_bf16(rng, (2, nb, 256, hkv, D))
+    gq, gk = wl.gamma_bf16(rng), wl.gamma_bf16(rng)
+    table = pkv.rope_cache_build(40960, D, 1e6, device=dev)
+    gq_d, gk_d = to_dev(gq, dev), to_dev(gk, dev)
+    qkv_d, pos_d, slot_d, ctx_d, bt_d = (to_dev(x, dev) for x in (qkv, pos, slots, ctx32, bt))
+
+    kc1, vc1 = to_dev(pool[0], dev), to_dev(pool[1], dev)
+    st = pkv.DecodeStep(qkv_d, kc1, vc1, pos_d, slot_d, ctx_d, bt_d, gq_d, gk_d, table, hq, hkv, eps=shape.eps)
+    st.run(batch)
+
+    kc2, vc2 = to_dev(pool[0], dev), to_dev(pool[1], dev)
+    q0, k0, v0 = hq * D, (hq + hkv) * D, width
+    qv = qkv_d[:, :q0].view(batch, hq, D)
+    kv = qkv_d[:, q0:k0].view(batch, hkv, D)
+    vv = qkv_d[:, k0:v0].view(batch, hkv, D)
+    q_out = pkv.qk_norm_rope_store(qv, kv, vv, pos_d, gq_d, gk_d, table, kc2, vc2, slot_d, eps=shape.eps)
+    o2 = pkv.attn_decode_paged(q_out, kc2, vc2, ctx_d, bt_d)
+    torch.cuda.synchronize()
+    assert torch.equal(st.q_out[:batch].view(torch.int16), q_out.view(torch.int16)), "q'"
+    assert torch.equal(kc1.view(torch.int16), kc2.view(torch.int16)), "k_cache"
+    assert torch.equal(vc1.view(torch.int16), vc2.view(torch.int16)), "v_cache"
+    assert torch.equal(st.o[:batch].view(torch.int16), o2.view(torch.int16)), "o"
+    st.close()
