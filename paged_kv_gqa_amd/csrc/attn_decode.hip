@@ -39,6 +39,10 @@
 //   * Each wave writes its split's (m, l, O) to a caller-owned fp32 workspace
 //     and a second kernel merges the splits of each (b, h) in split order
 //     (deterministic).
+//   * The decode step (launch_decode_step) runs QK-Norm + RoPE + scatter inside
+//     the split kernel: each workgroup normalises and rotates its own q rows,
+//     and the one holding a row's last chunk computes the new token's k' and v,
+//     stores them at the row's slot and patches them into that chunk.
 #include <mutex>
 
 #include "pkv_device.h"
@@ -551,6 +555,78 @@ __global__ void __launch_bounds__(64 * kCombineWaves) decode_combine_kernel(
     *reinterpret_cast<uint32_t*>(o + bh * kHeadDim + 2 * lane) = pack_bf16x2(r0, r1);
 }
 
+// Merge for many splits per (b, h) (a long context at a batch of one or two):
+// one workgroup per (b, h), wave w adding splits w, w + 4, ..., eight splits'
+// loads in flight, against the common reference max; the four waves' sums are
+// then added in wave order (deterministic).
+constexpr int kWideMergeSplits = 32;   // above this many splits per sequence, the wide merge
+__global__ void __launch_bounds__(256) decode_combine_wide_kernel(
+    const int32_t* __restrict__ context_lens, int32_t max_blocks, int32_t hq, int32_t split_chunks,
+    int32_t max_splits, const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    uint16_t* __restrict__ o) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int h = blockIdx.x, b = blockIdx.y;
+    __shared__ float s_m[4];
+    __shared__ float s_acc[4][3][64];
+    int ctx = context_lens[b];
+    const int cap = max_blocks * kBlockSize;
+    ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+    const int ns = ((ctx + kCK - 1) / kCK + split_chunks - 1) / split_chunks;
+    const int64_t bh = (int64_t)b * hq + h;
+    const float* ml = part_ml + bh * max_splits * 2;
+    const float* po = part_o + bh * max_splits * kHeadDim + 2 * lane;
+
+    float M = -INFINITY;
+    for (int s = wave + 4 * lane; s < ns; s += 256) M = fmaxf(M, ml[2 * s]);
+    M = wave_max(M);
+    if (lane == 0) s_m[wave] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    const float ref = M == -INFINITY ? 0.f : M;
+
+    constexpr int kF = 8;
+    float L = 0.f, acc0 = 0.f, acc1 = 0.f;
+    int s = wave;
+    for (; s + 4 * (kF - 1) < ns; s += 4 * kF) {
+        float2 p[kF];
+        float m[kF], l[kF];
+#pragma unroll
+        for (int i = 0; i < kF; ++i) {
+            p[i] = *reinterpret_cast<const float2*>(po + (int64_t)(s + 4 * i) * kHeadDim);
+            m[i] = ml[2 * (s + 4 * i)];
+            l[i] = ml[2 * (s + 4 * i) + 1];
+        }
+#pragma unroll
+        for (int i = 0; i < kF; ++i) {
+            const float w = exp2f(m[i] - ref);
+            L = fmaf(l[i], w, L);
+            acc0 = fmaf(p[i].x, w, acc0);
+            acc1 = fmaf(p[i].y, w, acc1);
+        }
+    }
+    for (; s < ns; s += 4) {
+        const float2 p = *reinterpret_cast<const float2*>(po + (int64_t)s * kHeadDim);
+        const float w = exp2f(ml[2 * s] - ref);
+        L = fmaf(ml[2 * s + 1], w, L);
+        acc0 = fmaf(p.x, w, acc0);
+        acc1 = fmaf(p.y, w, acc1);
+    }
+    s_acc[wave][0][lane] = L;
+    s_acc[wave][1][lane] = acc0;
+    s_acc[wave][2][lane] = acc1;
+    __syncthreads();
+    if (wave != 0) return;
+    float Lt = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        Lt += s_acc[w][0][lane];
+        a0 += s_acc[w][1][lane];
+        a1 += s_acc[w][2][lane];
+    }
+    const float r0 = Lt > 0.f ? a0 / Lt : 0.f, r1 = Lt > 0.f ? a1 / Lt : 0.f;
+    *reinterpret_cast<uint32_t*>(o + bh * kHeadDim + 2 * lane) = pack_bf16x2(r0, r1);
+}
+
 // ---- split-K workspace in a fixed device array, for pkv_attn_decode_paged_noalloc.
 // Callers that cannot allocate (code under graph capture, tight serving loops)
 // get the partials (m, l, O) and the dispatch order here instead of in a
@@ -622,9 +698,13 @@ hipError_t launch_decode_impl(const DecodeArgs& a, const StepArgs& sa, hipStream
 #undef PKV_DECODE_CASE
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3((a.hq + kCombineWaves - 1) / kCombineWaves, a.num_seqs),
-                       dim3(64 * kCombineWaves), 0, stream, a.context_lens,
-                       a.max_blocks, a.hq, sc, ms, w.part_o, w.part_ml, (uint16_t*)a.o);
+    if (ms > kWideMergeSplits)
+        hipLaunchKernelGGL(decode_combine_wide_kernel, dim3(a.hq, a.num_seqs), dim3(256), 0, stream, a.context_lens,
+                           a.max_blocks, a.hq, sc, ms, w.part_o, w.part_ml, (uint16_t*)a.o);
+    else
+        hipLaunchKernelGGL(decode_combine_kernel, dim3((a.hq + kCombineWaves - 1) / kCombineWaves, a.num_seqs),
+                           dim3(64 * kCombineWaves), 0, stream, a.context_lens,
+                           a.max_blocks, a.hq, sc, ms, w.part_o, w.part_ml, (uint16_t*)a.o);
     return hipGetLastError();
 }
 }  // namespace

@@ -57,6 +57,12 @@
 //     each such unit runs on one XCD (its K/V stays in that L2) and the units
 //     are dealt round-robin over the 8 XCDs (cut into 2-block chunks when there
 //     are fewer than 8), so unequal or few sequences balance.
+//   * Key split: when a call's query blocks do not fill the CU slots and keys
+//     run long (later chunks over a long cached context), the fast pass cuts
+//     each long block's key tiles into 2-4 chunks run by separate workgroups.
+//     The fixed reference makes their O and row sums simply add; a merge kernel
+//     adds them in chunk order (fp32, from the caller's workspace) and finishes
+//     as the fast pass does.
 #include <algorithm>
 #include <atomic>
 
