@@ -56,7 +56,8 @@
 //   * Work order: longest query blocks first inside each (sequence, kv head);
 //     each such unit runs on one XCD (its K/V stays in that L2) and the units
 //     are dealt round-robin over the 8 XCDs (cut into 2-block chunks when there
-//     are fewer than 8), so unequal or few sequences balance.
+//     are fewer than 8), so unequal or few sequences balance.  A small batch
+//     takes an XCD's units together, heaviest blocks of all of them first.
 //   * Key split: when a call's query blocks do not fill the CU slots and keys
 //     run long (later chunks over a long cached context), the fast pass cuts
 //     each long block's key tiles into 2-4 chunks run by separate workgroups.
@@ -95,6 +96,8 @@ constexpr int kSplitMinChunkTiles = 8;
 // lane (entry 64 * r + lane) and its partial row sum per lane.
 constexpr int kPartFloats = 64 * 64 + 64;
 constexpr size_t kSplitMaxBytes = size_t(512) << 20;
+constexpr int kWindowUnits = 8;                      // units per XCD dealt as one window, at most
+constexpr int64_t kWindowBytes = int64_t(8) << 20;    // their K/V, at most
 }  // namespace
 
 // Chunks of a work item of n_tiles key tiles when the call splits items into up to
@@ -637,26 +640,55 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, int32_t m_bl
     prefill_finish<!kExact>(a, call, cq0, Lq, wp0, head, wave_live, oacc, l_part);
 }
 
+// Work item of the kx-th workgroup of XCD xcd (XCDs take workgroups round-robin
+// by id).  Work items are numbered unit * m_blocks + i, where a unit is one
+// (sequence, kv head, head group) and i = 0 is its heaviest (last) query block.
+// With fewer units than XCDs (chunk < m_blocks) the items go out in chunks of 2
+// blocks, round-robin.  Otherwise XCD x runs units x, x+8, x+16, ..., so each
+// unit's K/V stays in one L2, taken `win` units at a time: within such a window
+// the 4 heaviest blocks of every unit come first, then the next 4, and so on.  A
+// window of one unit runs each unit's blocks in turn; wider windows let the long
+// sequences of a ragged batch start at once instead of after the units dealt
+// before them (the XCD dispatches in order, so a late heavy block is a late end).
+// Blocks of one unit dealt together: an XCD hands consecutive workgroups to its 4
+// shader engines in turn, so a group of 4 spreads each unit over all of them.
+constexpr int kDealGroup = 4;
+__device__ __forceinline__ int deal_item(int xcd, int kx, int chunk, int win, int m_blocks, int n_work) {
+    if (chunk < m_blocks || win <= 1) return (xcd + 8 * (kx / chunk)) * chunk + kx % chunk;
+    const int nu = (n_work / m_blocks + 7) / 8;    // units per XCD in the grid
+    const int span = win * m_blocks;
+    const int w = kx / span, r = kx - w * span;
+    const int ws = min(win, nu - w * win);          // units in this window (the last may be short)
+    if (ws <= 0) return n_work;                     // past the grid's items: none
+    // rounds of kDealGroup blocks per unit, so each unit's blocks still go to
+    // consecutive workgroup slots (spread over the XCD's shader engines)
+    const int full = m_blocks / kDealGroup, head = full * ws * kDealGroup;
+    int j, i;
+    if (r < head) {
+        const int round = r / (ws * kDealGroup), rr = r - round * ws * kDealGroup;
+        j = rr / kDealGroup;
+        i = round * kDealGroup + rr % kDealGroup;
+    } else {
+        const int last = m_blocks - full * kDealGroup, rr = r - head;
+        j = rr / last;
+        i = full * kDealGroup + rr % last;
+    }
+    return (xcd + 8 * (w * win + j)) * m_blocks + i;
+}
+
 // The two passes are separate kernels so that the exact pass's code does not
 // change how the compiler schedules the fast pass's loop.  The launcher runs the
 // fast pass, then the exact pass as a persistent kernel of at most one
 // workgroup per CU slot, which exits at once unless this call flagged something.
 template <int GW, bool PAGED, int NW>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a, int32_t m_blocks, int32_t n_work,
-                                                                  int32_t head_groups, int32_t chunk, uint64_t call,
-                                                                  int32_t nc, float* part) {
+                                                                  int32_t head_groups, int32_t chunk, int32_t win,
+                                                                  uint64_t call, int32_t nc, float* part) {
     constexpr int kKT = kTileKeys<NW>;
     __shared__ __attribute__((aligned(16))) unsigned char k_lds[2 * kKT * kHeadDim * 2];
     __shared__ __attribute__((aligned(16))) unsigned char v_lds[2 * kKT * kHeadDim * 2];
 
-    // Chunks of `chunk` consecutive work items are dealt round-robin over the 8
-    // XCDs, which take workgroups round-robin by id: XCD x runs chunks x, x+8,
-    // x+16, ... in order.  A chunk is one (sequence, kv head, head group) unit --
-    // all its query blocks, so its K/V stays in one L2 -- unless there are fewer
-    // units than XCDs; then it is two query blocks, so few sequences still spread
-    // over all XCDs.
-    //
-    // With a key split (nc > 1) the nc chunks of each item take consecutive slots of
+    // Work items by deal_item.  With a key split (nc > 1) the nc chunks of each item take consecutive slots of
     // its XCD, so they run side by side and share the item's K/V in one L2.
     const int xcd = blockIdx.x & 7;
     int kx = blockIdx.x >> 3, c = 0;
@@ -664,7 +696,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_kernel(PrefillArgs a,
         c = kx % nc;
         kx /= nc;
     }
-    const int work = (xcd + 8 * (kx / chunk)) * chunk + kx % chunk;
+    const int work = deal_item(xcd, kx, chunk, win, m_blocks, n_work);
     if (work >= n_work) return;
     prefill_block<GW, PAGED, NW, false>(a, m_blocks, head_groups, work, (lds_byte*)k_lds, (lds_byte*)v_lds, call, c,
                                         nc, part);
@@ -732,7 +764,8 @@ __global__ void __launch_bounds__(64) prefill_merge_kernel(PrefillArgs a, int32_
 template <int GW, bool PAGED, int NW>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_exact_kernel(PrefillArgs a, int32_t m_blocks,
                                                                         int32_t n_work, int32_t head_groups,
-                                                                        int32_t chunk, int32_t n_iter, uint64_t call) {
+                                                                        int32_t chunk, int32_t win, int32_t n_iter,
+                                                                        uint64_t call) {
     constexpr int kKT = kTileKeys<NW>;
     __shared__ __attribute__((aligned(16))) unsigned char k_lds[2 * kKT * kKPitch];
     __shared__ __attribute__((aligned(16))) unsigned char v_lds[2 * kKT * kVPitch];
@@ -742,7 +775,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) prefill_exact_kernel(PrefillA
     // Every workgroup walks the same item sequence, so the barriers inside match.
     for (int i = blockIdx.x; i < n_iter; i += gridDim.x) {
         const int xcd = i & 7, kx = i >> 3;
-        const int work = call != 0 ? i : (xcd + 8 * (kx / chunk)) * chunk + kx % chunk;
+        const int work = call != 0 ? i : deal_item(xcd, kx, chunk, win, m_blocks, n_work);
         if (work >= n_work) continue;
         prefill_block<GW, PAGED, NW, true>(a, m_blocks, head_groups, work, (lds_byte*)k_lds, (lds_byte*)v_lds, call);
     }
@@ -754,6 +787,7 @@ struct PrefillPlan {
     bool ok = false;
     int gw = 0, head_groups = 0, nw = 0, m_blocks = 0, n_work = 0, grid = 0, grid_exact = 0, n_iter = 0;
     int64_t chunk = 0;
+    int win = 1;               // units per dealing window (deal_item)
     bool wide = false, two_pass = false;
     int split_nc = 1;          // chunks per split item (1: no split)
     size_t split_bytes = 0;    // workspace the split needs
@@ -784,6 +818,17 @@ PrefillPlan plan_prefill(int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q
     const int64_t grid64 = ((n_chunks + 7) / 8) * 8 * p.chunk;
     if (grid64 > (int64_t)0x7FFFFFF0 / 4) return p;
     p.grid = (int)grid64;
+    // Dealing window (deal_item): an XCD share of at most kWindowUnits units whose
+    // K/V (at most max_seqlen_k keys each) fits in kWindowBytes is dealt as one
+    // window, so the long sequences of a small ragged batch start at once (the
+    // 0.6B varlen batch: 60 -> 56 us).  Larger shares keep one unit at a time:
+    // windows there cost 2-7% (16 x 2048, 64 x 512, 8B prefix hits) and up to 13%
+    // with long cached prefixes, as the units' K/V no longer share the L2.
+    if (p.chunk == p.m_blocks) {
+        const int64_t unit_bytes = std::max<int64_t>(max_seqlen_k, 1) * kHeadDim * 2 * 2;
+        const int64_t nu = (units + 7) / 8;
+        if (nu > 1 && nu <= kWindowUnits && nu * unit_bytes <= kWindowBytes) p.win = (int)nu;
+    }
     // Batches under 2e10 FLOP (counted without the causal half, so roughly under
     // 20 us of work) run the exact pass alone in one launch: there the second
     // launch of the two-pass scheme (~4 us when nothing is flagged) costs more than
@@ -833,6 +878,7 @@ hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t stream) {
     const int gw = p.gw, head_groups = p.head_groups, m_blocks = p.m_blocks, n_work = p.n_work, grid = p.grid;
     const int grid_exact = p.grid_exact, n_iter = p.n_iter;
     const int64_t chunk = p.chunk;
+    const int win = p.win;
     const bool wide = p.wide, two_pass = p.two_pass;
     // The key split runs only with a workspace of the planned size (else the call
     // runs unsplit, with the same results up to summation order).
@@ -851,12 +897,12 @@ hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t stream) {
     do {                                                                                                         \
         if (two_pass)                                                                                            \
             hipLaunchKernelGGL((prefill_kernel<GW_, PG_, NW_>), dim3(grid * nc), dim3(64 * NW_), 0, stream, a,   \
-                               m_blocks, n_work, head_groups, (int32_t)chunk, call, nc, part);                   \
+                               m_blocks, n_work, head_groups, (int32_t)chunk, win, call, nc, part);              \
         if (nc > 1)                                                                                              \
             hipLaunchKernelGGL((prefill_merge_kernel<GW_, PG_, NW_>), dim3(n_work * NW_), dim3(64), 0, stream,   \
                                a, m_blocks, n_work, head_groups, nc, part, call);                                \
         hipLaunchKernelGGL((prefill_exact_kernel<GW_, PG_, NW_>), dim3(grid_exact), dim3(64 * NW_), 0, stream,   \
-                           a, m_blocks, n_work, head_groups, (int32_t)chunk, n_iter, call);                      \
+                           a, m_blocks, n_work, head_groups, (int32_t)chunk, win, n_iter, call);                 \
     } while (0)
     if (gw == 4) {
         if (wide) {

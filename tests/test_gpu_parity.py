@@ -239,6 +239,22 @@ def test_prefill_zero_length_sequences(dev, lens_q, lens_k, paged):
     check_attn(f64(o), ref, "prefill with empty sequences")
 
 
+@pytest.mark.parametrize("lens,paged", [
+    ([700, 150, 333], False),                  # exact pass alone; 22 query blocks per unit (rounds of 4 and a tail of 2)
+    ([1500, 400, 1100], False),                # fast + exact pass; 47 blocks per unit (tail of 3)
+    ([90, 1800, 5, 640, 1210, 0, 333], True),  # seven units per XCD, one sequence empty, over the paged cache
+])
+def test_prefill_small_ragged_batches_dealt_in_windows(dev, lens, paged):
+    """Small ragged batches (at most 8 units per XCD, little K/V) deal each XCD's units
+    together, heaviest query blocks of all of them first, in rounds of 4 blocks per unit.
+    Every row of every sequence is still computed once: all rows against the oracle."""
+    _say(f"prefill small ragged batch in dealing windows: lengths {lens}, paged={paged}")
+    lens_k = [l + 64 * i for i, l in enumerate(lens)] if paged else lens
+    o, ref, _ = _prefill_case(dev, lens, lens_k, 32, 8, seed=59 + len(lens), paged=paged)
+    assert o.shape[0] == sum(lens)
+    check_attn(f64(o), ref, "prefill in dealing windows")
+
+
 def test_cache_offsets_past_2_31_elements(dev):
     """A 9000-block pool (4.7 GB per cache at 8 kv heads): blocks past 8192 start beyond
     2^31 elements, so every cache address must be formed in 64 bits.  The same contents
