@@ -98,6 +98,7 @@ CASES = [
     ([256, 256], [8192, 8192], 16, 8, False),   # contiguous K/V with a long prefix, G = 2, 4 chunks
     ([2048], [16384], 8, 2, True),              # 8-wave kernel (mean query length 2048), G = 4, 4 chunks
     ([512, 512], [12288, 9000], 8, 8, True),    # G = 1, unequal contexts (a partial last tile)
+    ([128] * 8, [2048] * 8, 32, 8, True),       # 2 chunks, and the 8 units of each XCD dealt as one window
 ]
 
 
