@@ -286,6 +286,7 @@ def main():
     ladder = decode_graph_ladder(pkv, torch, s8, table, qkv_d, kc_d, vc_d, pos_d, slot_d, cl_d, bt_d, gq_d, gk_d,
                                  args, log)
     ladder_short = decode_graph_short(pkv, torch, dev, to_dev, table, args, log)
+    stack = decode_graph_stack(pkv, torch, dev, to_dev, table, args, log)
 
     cpu = cpu_pre = cpu_st = cpu_one = None
     if not args.no_cpu_baseline:
@@ -335,6 +336,7 @@ def main():
         "qwen3_0_6b": small,
         "decode_graph": ladder,
         "decode_graph_short": ladder_short,
+        "decode_graph_stack": stack,
         "cpu_baseline_prefill": cpu_pre,
         "cpu_baseline_stages": cpu_st,
         "cpu_baseline_one_thread": cpu_one,
@@ -613,6 +615,61 @@ def decode_graph_short(pkv, torch, dev, to_dev, table, args, log):
     stl.close()
     log(f"decode graph, short contexts (us/step): {json.dumps(out)}")
     del kc, vc
+    return out
+
+
+def decode_graph_stack(pkv, torch, dev, to_dev, table, args, log, layers=36, batches=(1, 4, 16, 64)):
+    """A layer stack of decode steps (Qwen3-8B has 36 layers, each with its own KV cache) on short
+    contexts (contexts U[256, 1024], 32/8 heads), eager (2 launches per layer) against one HIP graph
+    holding all layers' steps, captured through torch: latency (launch, then synchronise) and
+    back_to_back, both per layer."""
+    import workloads as wl
+    w = wl.short_decode_8b(args.seed)
+    s8 = w.shape
+    kc0 = torch.empty((w.num_blocks, 256, s8.num_kv_heads, 128), dtype=torch.bfloat16, device=dev)
+    vc0 = torch.empty_like(kc0)
+    wl.fill_normal_bf16_(kc0, 6, args.seed, 10)
+    wl.fill_normal_bf16_(vc0, 6, args.seed, 11)
+    qkv = to_dev(w.qkv())
+    gq, gk = (to_dev(g) for g in w.gammas())
+    pos, slot = to_dev(w.positions), to_dev(w.slot_mapping)
+    cl, bt = to_dev(w.context_lens), to_dev(w.block_tables)
+    caches = [(kc0.clone(), vc0.clone()) for _ in range(layers)]
+    steps = [pkv.DecodeStep(qkv, kc, vc, pos, slot, cl, bt, gq, gk, table, s8.num_q_heads, s8.num_kv_heads,
+                            eps=s8.eps) for kc, vc in caches]
+    reps = max(args.steps, 20)
+    out = {"workload": f"{layers} layers, each its own KV cache; {w.batch} sequences of the 8B shapes, contexts "
+                       f"U[256, 1024]; per layer: qk_norm_rope_store + paged decode", "layers": layers,
+           "unit": "us/layer", "latency": {"eager": {}, "graph": {}}, "back_to_back": {"eager": {}, "graph": {}}}
+    for b in batches:
+        def eager(b=b):
+            for st in steps:
+                st.run(b)
+        g = torch.cuda.CUDAGraph()
+        eager()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            eager()
+        torch.cuda.synchronize()
+        for mode, fn in (("eager", eager), ("graph", g.replay)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                fn()
+                torch.cuda.synchronize()
+            out["latency"][mode][str(b)] = round((time.perf_counter() - t0) * 1e6 / reps / layers, 2)
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                fn()
+            torch.cuda.synchronize()
+            out["back_to_back"][mode][str(b)] = round((time.perf_counter() - t0) * 1e6 / reps / layers, 2)
+        del g
+    for st in steps:
+        st.close()
+    log(f"decode layer stack, eager vs one graph (us/layer): {json.dumps(out)}")
+    del caches, kc0, vc0
     return out
 
 

@@ -213,3 +213,58 @@ def test_decode_step_equals_the_two_calls(dev, hq, hkv, batch, max_ctx):
     assert torch.equal(vc1.view(torch.int16), vc2.view(torch.int16)), "v_cache"
     assert torch.equal(st.o[:batch].view(torch.int16), o2.view(torch.int16)), "o"
     st.close()
+
+
+def test_decode_steps_captured_by_the_caller_in_one_graph(dev):
+    """A caller may capture several decode steps (here three layers, each with its own
+    caches) into one graph of its own through torch: every replay (torch work and host
+    synchronisations between them) gives, byte for byte, the eager steps' q', o and caches."""
+    shape, hq, hkv, batch, layers = wl.QWEN3_0_6B, 16, 8, 5, 3
+    _say(f"decode steps of {layers} layers captured into one caller graph, batch {batch}")
+    rng = wl.rng_for(97, 0, 0)
+    max_ctx, width = 900, (hq + 2 * hkv) * D
+    mb = -(-max_ctx // 256)
+    nb = batch * mb + 2
+    bt = rng.permutation(nb)[:batch * mb].reshape(batch, mb).astype(np.int32)
+    ctx = rng.integers(1, max_ctx, size=batch).astype(np.int64)
+    pos = ctx - 1
+    slots = np.array([bt[i, pos[i] // 256] * 256 + pos[i] % 256 for i in range(batch)], np.int32)
+    table = pkv.rope_cache_build(40960, D, 1e6, device=dev)
+    qkv_d = to_dev(wl.normal_bf16(rng, (batch, width)), dev)
+    gq_d, gk_d = to_dev(wl.gamma_bf16(rng), dev), to_dev(wl.gamma_bf16(rng), dev)
+    pos_d, slot_d, ctx_d, bt_d = (to_dev(x, dev) for x in (pos, slots, ctx.astype(np.int32), bt))
+    pools = [wl.normal_bf16(rng, (2, nb, 256, hkv, D)) for _ in range(layers)]
+
+    def make():
+        caches = [(to_dev(p[0], dev), to_dev(p[1], dev)) for p in pools]
+        steps = [pkv.DecodeStep(qkv_d, kc, vc, pos_d, slot_d, ctx_d, bt_d, gq_d, gk_d, table, hq, hkv, eps=shape.eps)
+                 for kc, vc in caches]
+        return caches, steps
+
+    ref_caches, ref_steps = make()
+    for st in ref_steps:
+        st.run(batch)
+    torch.cuda.synchronize()
+
+    caches, steps = make()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for st in steps:
+            st.run(batch)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(layers):
+            assert torch.equal(steps[i].q_out[:batch].view(torch.int16), ref_steps[i].q_out[:batch].view(torch.int16)), \
+                f"q' layer {i} replay {rep}"
+            assert torch.equal(steps[i].o[:batch].view(torch.int16), ref_steps[i].o[:batch].view(torch.int16)), \
+                f"o layer {i} replay {rep}"
+            for c, rc in zip(caches[i], ref_caches[i]):
+                assert torch.equal(c.view(torch.int16), rc.view(torch.int16)), f"cache layer {i} replay {rep}"
+        for st in steps:                      # eager work between the replays overwrites the outputs
+            st.o.zero_()
+            st.q_out.zero_()
+        torch.cuda.synchronize()
+    for st in steps + ref_steps:
+        st.close()
