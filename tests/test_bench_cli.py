@@ -33,6 +33,23 @@ def test_recorded_traffic_follows_the_kernel_source(tmp_path, monkeypatch):
     assert bench.recorded_traffic("missing.md", "k.hip") is None
 
 
+def test_recorded_traffic_is_one_call_of_the_workload():
+    """Each committed traffic figure is that of one call of the timed workload: the
+    measured HBM bytes sit just above the bytes the call must move (decode: the
+    unique K/V bytes; prefill: q, o and every cached K/V byte once), not a sum over
+    several calls or workloads."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import workloads as wl
+    dec = bench.recorded_traffic("attn_decode_paged_qwen3_8b_hbm_traffic.md", "attn_decode.hip")
+    alg = wl.paged_decode_8b(0).algorithmic_bytes(True)
+    assert 1.0 <= dec / alg <= 1.1, f"decode traffic {dec} is {dec / alg:.3f}x the call's bytes"
+    wp = wl.prefix_prefill_8b(0)
+    compulsory = wp.num_q_tokens * 32 * 128 * 2 * 2 + (wp.prefix_len + wp.num_seqs * wp.suffix_len) * 8 * 128 * 2 * 2
+    pre = bench.recorded_traffic("attn_prefill_qwen3_8b_prefix_hbm_traffic.md", "attn_prefill.hip")
+    assert 1.0 <= pre / compulsory <= 1.5, f"prefill traffic {pre} is {pre / compulsory:.3f}x the compulsory bytes"
+
+
 def test_input_checksum_sees_every_word():
     """The checksum recorded beside the seed changes when any one input word changes,
     and not when nothing does."""
