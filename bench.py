@@ -97,6 +97,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ladders", action="store_true",
+                    help="skip the decode-step graph measurements (ladders and the layer stack), as the "
+                         "counter runs behind profiles/ do")
     ap.add_argument("--cpu-seqs", type=int, default=256, help="decode sequences the oracle times")
     ap.add_argument("--cpu-prefill-rows", type=int, default=131072, help="prefill (token, head) rows the oracle times")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -283,10 +286,12 @@ def main():
     small = qwen3_0_6b_shapes(pkv, torch, dev, to_dev, args, log)
     copy_ref = copy_reference(torch, dev, log)
 
-    ladder = decode_graph_ladder(pkv, torch, s8, table, qkv_d, kc_d, vc_d, pos_d, slot_d, cl_d, bt_d, gq_d, gk_d,
-                                 args, log)
-    ladder_short = decode_graph_short(pkv, torch, dev, to_dev, table, args, log)
-    stack = decode_graph_stack(pkv, torch, dev, to_dev, table, args, log)
+    ladder = ladder_short = stack = None
+    if not args.no_ladders:
+        ladder = decode_graph_ladder(pkv, torch, s8, table, qkv_d, kc_d, vc_d, pos_d, slot_d, cl_d, bt_d, gq_d, gk_d,
+                                     args, log)
+        ladder_short = decode_graph_short(pkv, torch, dev, to_dev, table, args, log)
+        stack = decode_graph_stack(pkv, torch, dev, to_dev, table, args, log)
 
     cpu = cpu_pre = cpu_st = cpu_one = None
     if not args.no_cpu_baseline:

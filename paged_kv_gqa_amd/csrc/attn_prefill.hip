@@ -40,8 +40,9 @@
 //     rows (16-byte copies; rows past the last key clamped, V zeroed there).
 //   * Softmax in two passes.  The fast pass (one kernel) takes exp2 of each
 //     score times softmax_scale * log2(e) (fp32) against a fixed reference of
-//     0: no row max, no rescale, four VALU operations per score (multiply,
-//     exp2, add, half a bf16 pack) instead of five.  The reference cancels in
+//     0: no row max and no rescale; per score a multiply, an exp2 and halves
+//     of a bf16 pack and of the row-sum dot2 (the exact pass adds the max and
+//     an fma against it).  The reference cancels in
 //     O / l and floating point is scale-invariant away from its range limits,
 //     so the weights are the online softmax's up to fp32 rounding while a
 //     row's weights stay far from overflow and underflow; a wave whose rows
