@@ -236,12 +236,22 @@ int pkv_attn_prefill_varlen(const void* q, int64_t q_row_stride, const void* k, 
     if (workspace && workspace_bytes) {
         PKV_REQUIRE((uintptr_t)workspace % 256 == 0, PKV_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned",
                     fn);
-        // the split writes partial sums while q is read and o written
-        const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + workspace_bytes;
+        // the split writes partial sums while q and the keys are read and o written;
+        // it uses at most the first 512 MiB (pkv_attn_prefill_workspace_bytes)
+        const size_t used = workspace_bytes < (size_t(512) << 20) ? workspace_bytes : (size_t(512) << 20);
+        const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + used;
+        PKV_REQUIRE(w1 > w0, PKV_ERR_WORKSPACE, "%s: workspace range wraps the address space", fn);
         const uintptr_t q0 = (uintptr_t)q, q1 = q0 + (uintptr_t)(((int64_t)(total_q - 1) * q_row_stride + qw) * 2);
         const uintptr_t o0 = (uintptr_t)o, o1 = o0 + (uintptr_t)((int64_t)total_q * qw * 2);
         PKV_REQUIRE((w1 <= q0 || q1 <= w0) && (w1 <= o0 || o1 <= w0), PKV_ERR_WORKSPACE,
                     "%s: workspace must not overlap q or o", fn);
+        if (block_table && num_blocks > 0) {
+            // the caches' extent is known here (num_blocks slots of block_size rows)
+            const uintptr_t cache_bytes = (uintptr_t)num_blocks * (uintptr_t)block_size * (uintptr_t)kw * 2;
+            const uintptr_t k0 = (uintptr_t)k, v0 = (uintptr_t)v;
+            PKV_REQUIRE((w1 <= k0 || k0 + cache_bytes <= w0) && (w1 <= v0 || v0 + cache_bytes <= w0),
+                        PKV_ERR_WORKSPACE, "%s: workspace must not overlap the caches", fn);
+        }
     }
     if (block_table) {
         PKV_REQUIRE(block_size == 256, PKV_ERR_UNSUPPORTED, "%s: block_size %d unsupported (only 256)", fn,

@@ -105,6 +105,12 @@ def test_prefill_validation(lib):
     assert f(*a) == -4 and "aligned" in _err(lib)
     a = list(base); a[22] = ctypes.c_void_p(o_fake); a[23] = 1 << 20   # workspace on top of o
     assert f(*a) == -4 and "overlap" in _err(lib)
+    paged = list(base); paged[18] = FAKE; paged[3] = paged[5] = 1024; paged[19] = 2; paged[21] = 8
+    cache_end = FAKE.value + 8 * 256 * 1024 * 2
+    a = list(paged); a[22] = ctypes.c_void_p(cache_end - 256); a[23] = 1 << 20   # workspace over the caches' tail
+    assert f(*a) == -4 and "caches" in _err(lib)
+    a = list(base); a[22] = ctypes.c_void_p(((1 << 64) - (1 << 20)) & ~255); a[23] = 2 << 20   # wraps
+    assert f(*a) == -4 and "wraps" in _err(lib)
 
 
 def test_prefill_workspace_query(lib):
