@@ -253,7 +253,8 @@ PKV_API size_t pkv_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_h
  *   context_lens      int32 [num_seqs], each <= max_blocks_per_seq * block_size.
  *   block_table       int32 [num_seqs][max_blocks_per_seq], -1 padded.
  *   workspace         device scratch of at least
- *                     pkv_attn_decode_workspace_bytes(...) bytes, 256-byte aligned;
+ *                     pkv_attn_decode_workspace_bytes(...) bytes, 256-byte aligned,
+ *                     sharing no byte with q, o or the caches (else PKV_ERR_WORKSPACE);
  *                     owned by the caller, contents need no initialisation.
  * The split of each context into chunks and their merge are deterministic:
  * the result does not depend on where the blocks sit in the pool.

@@ -308,6 +308,25 @@ size_t pkv_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
 }
 
 namespace {
+// True when the byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return na && nb && a0 < b0 + nb && b0 < a0 + na;
+}
+
+// The decode workspace (written by the split kernel while q and the caches are read,
+// then read by the merge while o is written) must not share bytes with them.
+int decode_workspace_check(const char* fn, const void* ws, size_t need, const void* q, const void* o,
+                           const void* k_cache, const void* v_cache, int32_t rows, int32_t num_q_heads,
+                           int32_t num_kv_heads, int64_t num_blocks) {
+    const size_t qo = (size_t)rows * num_q_heads * 128 * 2;
+    const size_t cache = (size_t)num_blocks * 256 * num_kv_heads * 128 * 2;
+    PKV_REQUIRE(!overlaps(ws, need, q, qo) && !overlaps(ws, need, o, qo) && !overlaps(ws, need, k_cache, cache) &&
+                    !overlaps(ws, need, v_cache, cache),
+                PKV_ERR_WORKSPACE, "%s: workspace must not overlap q, o or the caches", fn);
+    return PKV_OK;
+}
+
 // Checks shared by the two decode entry points; on success fills `a` (workspace unset).
 int decode_args(const char* fn, const void* q, const void* k_cache, const void* v_cache, void* o,
                 const int32_t* context_lens, const int32_t* block_table, int32_t max_blocks_per_seq, int32_t num_seqs,
@@ -362,6 +381,9 @@ int pkv_attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
     PKV_REQUIRE(workspace != nullptr && workspace_bytes >= need, PKV_ERR_WORKSPACE,
                 "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? workspace_bytes : (size_t)0);
     PKV_REQUIRE((uintptr_t)workspace % 256 == 0, PKV_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+    rc = decode_workspace_check(fn, workspace, need, q, o, k_cache, v_cache, num_seqs, num_q_heads, num_kv_heads,
+                                num_blocks);
+    if (rc) return rc;
     a.workspace = workspace;
     return launched(pkv::launch_attn_decode(a, (hipStream_t)stream), fn);
 }
@@ -395,6 +417,11 @@ int decode_step_run(const pkv_decode_step_desc& d, int32_t batch, hipStream_t st
                 "pkv_decode_step: workspace of %zu bytes needed, %zu given", need,
                 d.workspace ? d.workspace_bytes : (size_t)0);
     PKV_REQUIRE((uintptr_t)d.workspace % 256 == 0, PKV_ERR_WORKSPACE, "pkv_decode_step: workspace must be 256-byte aligned");
+    rc = decode_workspace_check("pkv_decode_step", d.workspace, need, d.q_out, d.o, d.k_cache, d.v_cache, batch,
+                                d.num_q_heads, d.num_kv_heads, d.num_blocks);
+    if (rc) return rc;
+    PKV_REQUIRE(!overlaps(d.workspace, need, d.qkv, (size_t)batch * d.qkv_row_stride * 2), PKV_ERR_WORKSPACE,
+                "pkv_decode_step: workspace must not overlap qkv");
     a.workspace = d.workspace;
     pkv::StepArgs sa;
     sa.qkv = qkv;

@@ -149,6 +149,13 @@ def test_decode_validation_and_workspace(lib):
     assert f(*a) == -1
     a = list(base); a[7] = 0                          # empty batch
     assert f(*a) == 0
+    far = ctypes.c_void_p(1 << 40)                    # q, caches and o away from the workspace
+    ok = [far, ctypes.c_void_p((1 << 40) + (1 << 30)), ctypes.c_void_p((1 << 40) + (2 << 30)),
+          ctypes.c_void_p((1 << 40) + (3 << 30))] + base[4:]
+    a = list(ok); a[14] = ctypes.c_void_p((1 << 40) + (1 << 30) + (1 << 20))   # inside k_cache
+    assert f(*a) == -4 and "overlap" in _err(lib)
+    a = list(ok); a[14] = ctypes.c_void_p(((1 << 40) + (3 << 30) - 256))      # running into o
+    assert f(*a) == -4 and "overlap" in _err(lib)
 
 
 def test_qk_norm_rope_store_validation(lib):
