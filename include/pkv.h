@@ -233,7 +233,10 @@ PKV_API size_t pkv_attn_prefill_workspace_bytes(int32_t num_seqs, int32_t total_
 
 /*
  * pkv_attn_decode_workspace_bytes -- device workspace pkv_attn_decode_paged
- * needs for these sizes (0 on invalid sizes).  Host-only, no HIP call.
+ * needs for these sizes (0 on invalid sizes, and on sizes past the launch grid:
+ * more than 65535 sequences, or tables so long that a sequence would need more
+ * than 65535 splits; the decode calls refuse those with PKV_ERR_UNSUPPORTED).
+ * Host-only, no HIP call.
  */
 PKV_API size_t pkv_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size);

@@ -341,6 +341,10 @@ int decode_args(const char* fn, const void* q, const void* k_cache, const void* 
     PKV_REQUIRE(num_seqs >= 0, PKV_ERR_INVALID_ARG, "%s: num_seqs must be >= 0", fn);
     PKV_REQUIRE(max_blocks_per_seq > 0, PKV_ERR_INVALID_ARG, "%s: max_blocks_per_seq must be > 0", fn);
     if (num_seqs == 0) return PKV_OK;
+    PKV_REQUIRE(pkv_attn_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                                                block_size) > 0,
+                PKV_ERR_UNSUPPORTED, "%s: %d sequences of up to %d blocks exceed the launch grid", fn, num_seqs,
+                max_blocks_per_seq);
     PKV_REQUIRE(q && k_cache && v_cache && o && context_lens && block_table, PKV_ERR_INVALID_ARG,
                 "%s: a required pointer is NULL", fn);
     PKV_REQUIRE(k_cache != v_cache, PKV_ERR_INVALID_ARG, "%s: k_cache and v_cache must be distinct", fn);

@@ -87,6 +87,7 @@ constexpr int kMinSplitChunks = PKV_DECODE_MIN_CHUNKS;   // shortest split (16-k
 #endif
 constexpr int kMaxSplits = PKV_DECODE_MAX_SPLITS;        // splits per sequence the sub-block lengths allow
 constexpr int kResidentItems = 512;                      // split workgroups the chip holds at once (2 per CU)
+constexpr int64_t kMaxGridYZ = 65535;                    // largest y / z extent of a launch grid
 
 struct Workspace {
     float* part_o;   // [B][Hq][S][128]
@@ -133,8 +134,12 @@ int decode_split_chunks(int32_t num_seqs, int32_t hkv, int32_t max_blocks) {
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t max_blocks) {
     const int sc = decode_split_chunks(num_seqs, hkv, max_blocks);
     const int64_t ms = ((int64_t)max_blocks * (kBlockSize / kCK) + sc - 1) / sc;
-    const size_t o_bytes = align256((size_t)num_seqs * hq * ms * kHeadDim * sizeof(float));
-    const size_t ml_bytes = align256((size_t)num_seqs * hq * ms * 2 * sizeof(float));
+    // the split grid is (kv head groups, num_seqs, ms): its y and z extents are at most 65535
+    if (num_seqs > kMaxGridYZ || ms > kMaxGridYZ) return 0;
+    const unsigned __int128 rows = (unsigned __int128)num_seqs * (unsigned)hq * (uint64_t)ms;
+    if (rows * (kHeadDim + 2) * sizeof(float) > ((unsigned __int128)1 << 48)) return 0;   // beyond any device
+    const size_t o_bytes = align256((size_t)rows * kHeadDim * sizeof(float));
+    const size_t ml_bytes = align256((size_t)rows * 2 * sizeof(float));
     const size_t work_bytes = align256((size_t)num_seqs * ms * sizeof(int32_t));
     return o_bytes + ml_bytes + work_bytes;
 }

@@ -807,7 +807,7 @@ PrefillPlan plan_prefill(int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q
     p.wide = p.gw >= 2 && (int64_t)total_q >= (int64_t)2048 * num_seqs;
     p.nw = p.wide ? 8 : 4;
     const int bm = kRowsPerWave * (p.nw / p.gw);
-    p.m_blocks = (max_seqlen_q + bm - 1) / bm;
+    p.m_blocks = (int)(((int64_t)max_seqlen_q + bm - 1) / bm);
     const int64_t n_work64 = (int64_t)num_seqs * hkv * p.head_groups * p.m_blocks;
     if (n_work64 > (int64_t)0x7FFFFFF0) return p;
     p.n_work = (int)n_work64;
@@ -852,7 +852,7 @@ PrefillPlan plan_prefill(int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q
     // items for 512 slots) is left whole: split, it ran 59.5 -> 87 us.
     const int kt = p.nw == 8 ? 128 : 64;
     const int64_t max_tiles = ((int64_t)max_seqlen_k + kt - 1) / kt;
-    const int64_t n_real = ((int64_t)(total_q + bm - 1) / bm + num_seqs) * hkv * p.head_groups;
+    const int64_t n_real = (((int64_t)total_q + bm - 1) / bm + num_seqs) * hkv * p.head_groups;
     if (p.two_pass && n_real <= slots && max_tiles >= 2 * kSplitMinChunkTiles) {
         const int nc = (int)std::min<int64_t>(4, slots / std::max<int64_t>(n_real, 1) + 1);
         const size_t bytes = (size_t)p.n_work * nc * p.nw * kPartFloats * sizeof(float);

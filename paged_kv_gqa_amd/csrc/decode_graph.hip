@@ -79,10 +79,20 @@ extern "C" {
 size_t pkv_decode_step_workspace_bytes(int32_t max_batch, int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size) {
     if (max_batch <= 0) return 0;
+    // The split length depends on the batch only while it has fewer than ~1400 split
+    // items; from 4096 sequences on it is fixed and the workspace grows with the
+    // batch, so its largest value is at max_batch.
     size_t best = 0;
-    for (int32_t b = 1; b <= max_batch; ++b) {
+    const int32_t last = max_batch < 4096 ? max_batch : 4096;
+    for (int32_t b = 1; b <= last; ++b) {
         const size_t w = pkv_attn_decode_workspace_bytes(b, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
                                                          block_size);
+        if (w == 0) return 0;
+        if (w > best) best = w;
+    }
+    if (max_batch > last) {
+        const size_t w = pkv_attn_decode_workspace_bytes(max_batch, num_q_heads, num_kv_heads, head_dim,
+                                                         max_blocks_per_seq, block_size);
         if (w == 0) return 0;
         if (w > best) best = w;
     }
