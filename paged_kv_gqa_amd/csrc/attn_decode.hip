@@ -236,19 +236,24 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
     const int g = 4 * blockIdx.x + wave, b = item / max_splits, s = item - b * max_splits;
     if (g >= hkv) return;
 
+    // The split covers the context's 16-key chunks c0 .. c0 + nchunks - 1, all for
+    // this wave; they lie in blocks blk0 .. blk0 + nb - 1.  The table entries the
+    // split can touch follow from s alone, so they are loaded beside the context
+    // length instead of after it (one memory round trip less before the first K/V).
+    constexpr int kCPB = kBlockSize / kCK;           // chunks per block
+    const int c0 = s * split_chunks;
+    const int blk0 = c0 / kCPB;
+    int raw_blk = -1;
+    if (lane < (split_chunks + kCPB - 1) / kCPB + 1 && blk0 + lane < max_blocks)
+        raw_blk = block_table[(int64_t)b * max_blocks + blk0 + lane];
     int ctx = context_lens[b];
     const int cap = max_blocks * kBlockSize;
     ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
-    // The split covers the context's 16-key chunks c0 .. c0 + nchunks - 1, all for
-    // this wave; they lie in blocks blk0 .. blk0 + nb - 1.
-    constexpr int kCPB = kBlockSize / kCK;           // chunks per block
     const int nchk = (ctx + kCK - 1) / kCK;
-    const int c0 = s * split_chunks;
     // In a step, split 0 of every row also writes the row's q' (and, with an empty
     // context, stores the new token), so it runs even when it has no keys.
     if (c0 >= nchk && !(kStep && s == 0)) return;
     const int nchunks = c0 < nchk ? min(split_chunks, nchk - c0) : 0;
-    const int blk0 = c0 / kCPB;
     const int nb = nchunks > 0 ? (c0 + nchunks - 1) / kCPB - blk0 + 1 : 0;
 
     constexpr int kVPitch = kHeadDim * 2 + 32;       // bytes per V row in LDS (conflict-free transposed reads)
@@ -257,11 +262,7 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
     const int64_t row = (int64_t)hkv * kHeadDim;    // elements between consecutive cache rows
 
     // Block ids of this split, one per lane (lanes >= nb hold -1).
-    int my_blk = -1;
-    if (lane < nb) {
-        const int32_t id = block_table[(int64_t)b * max_blocks + blk0 + lane];
-        my_blk = (id >= 0 && (int64_t)id < num_blocks) ? id : -1;
-    }
+    const int my_blk = (lane < nb && raw_blk >= 0 && (int64_t)raw_blk < num_blocks) ? raw_blk : -1;
 
     // Lane (col, grp): col = head column of both products, grp = 4-key group.
     const int col = lane & 15, grp = lane >> 4;
