@@ -848,8 +848,9 @@ PrefillPlan plan_prefill(int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q
     // into slots / items + 1 chunks (2 to 4), whose partial sums a merge kernel
     // adds.  Measured on 4 x 256 queries over 16384 cached keys at 32/8 heads (288
     // items): 322 -> 279 us per call with two chunks (dealing every unit's heaviest
-    // block first on top of that: no change).  The 0.6B varlen batch (984
-    // items for 512 slots) is left whole: split, it ran 59.5 -> 87 us.
+    // block first on top of that: no change).  The 0.6B varlen batch (944
+    // items for 512 slots) is left whole: split in two, it ran 56 -> 69 us (the
+    // merge over all its items alone takes 9 us).
     const int kt = p.nw == 8 ? 128 : 64;
     const int64_t max_tiles = ((int64_t)max_seqlen_k + kt - 1) / kt;
     const int64_t n_real = (((int64_t)total_q + bm - 1) / bm + num_seqs) * hkv * p.head_groups;
