@@ -364,6 +364,19 @@ def test_prefill_long_sequences_wide_workgroups(dev, lens, hq, hkv):
     check_attn(f64(o2)[rows[:, 0], rows[:, 1]], ref2, "prefill long paged, 8 waves")
 
 
+@pytest.mark.parametrize("lq,lk,hq,hkv", [([1024, 1300, 1111], [3000, 2700, 5000], 32, 8),
+                                           ([1024, 1024], [2048, 2048], 64, 8),
+                                           ([1500, 800, 1100], [4000, 900, 3100], 8, 2)])
+def test_prefill_prefix_hits_medium_queries_wide_workgroups(dev, lq, lk, hq, hkv):
+    """Four q heads a workgroup, 1024+ query positions on average and cached prefixes
+    (longest key range at least twice the longest query): 8-wave workgroups."""
+    assert sum(lq) >= 1024 * len(lq) and max(lk) >= 2 * max(lq) and hq // hkv >= 4
+    _say(f"prefill case 2, queries {lq} over keys {lk}, {hq}/{hkv} heads (8-wave workgroups, prefix hits)")
+    rows = np.stack([np.arange(0, sum(lq), 5), np.arange(0, sum(lq), 5) % hq], 1)
+    o, ref, _ = _prefill_case(dev, lq, lk, hq, hkv, seed=sum(lq) + hq, paged=True, rows=rows)
+    check_attn(f64(o)[rows[:, 0], rows[:, 1]], ref, "prefill prefix hits, 8 waves")
+
+
 @pytest.mark.parametrize("lens,hq,hkv", [([1500], 4, 1), ([700, 90, 333], 4, 2), ([257], 8, 1)])
 def test_prefill_few_work_units(dev, lens, hq, hkv):
     """Fewer (sequence, kv head) units than XCDs: the work is dealt in 2-block chunks."""
