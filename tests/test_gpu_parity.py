@@ -689,6 +689,17 @@ def test_decode_long_context_many_splits(dev):
     check_attn(f64(r["o"]), r["ref"], "decode long")
 
 
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (64, 4)])
+def test_decode_longest_context(dev, hq, hkv):
+    """Qwen3's longest context (40960 positions, the length of its RoPE table), one short of it,
+    and one token: one-block splits, more than 32 of them per sequence (the wide merge), the
+    size-ordered grid; every row against the oracle, GQA groups of 4 and 16."""
+    ctx = [40960, 40959, 1]
+    _say(f"decode contexts {ctx}, {hq}/{hkv} heads")
+    r = _decode_case(dev, ctx, hq, hkv, seed=31 + hq)
+    check_attn(f64(r["o"]), r["ref"], "decode longest context")
+
+
 def test_decode_large_batch_short_contexts(dev):
     """1500 sequences: the split-item sort and the grid loop over more items than threads."""
     rng = wl.rng_for(97, 0, 0)
@@ -700,6 +711,28 @@ def test_decode_large_batch_short_contexts(dev):
     live = np.array(ctx) > 0
     check_attn(got[live], r["ref"][live], "decode large batch")
     assert np.all(got[~live] == 0.0)
+
+
+def test_prefill_longest_context(dev):
+    """One sequence of Qwen3's longest context (40960 tokens) at 32/8 heads, fresh, then its last
+    2048 tokens as new queries over the paged cache; rows at both ends, at tile and 2^15
+    boundaries, and at random, against the oracle."""
+    L = 40960
+    rng = wl.rng_for(93, 1, 0)
+    pick = [0, 1, 63, 64, 127, 128, 32767, 32768, L - 129, L - 128, L - 2, L - 1]
+    rows = [[p, h] for p in pick for h in (0, 31)]
+    rows += np.stack([rng.integers(0, L, 96), rng.integers(0, 32, 96)], 1).tolist()
+    rows = np.array(rows, np.int64)
+    _say(f"prefill case 1, one sequence of {L} tokens, 32/8 heads")
+    o, ref, _ = _prefill_case(dev, [L], [L], 32, 8, seed=L, rows=rows)
+    check_attn(f64(o)[rows[:, 0], rows[:, 1]], ref, "prefill longest context")
+    lq = 2048
+    rows2 = [[p, h] for p in (0, 1, 127, 128, 1024, lq - 2, lq - 1) for h in (0, 31)]
+    rows2 += np.stack([rng.integers(0, lq, 64), rng.integers(0, 32, 64)], 1).tolist()
+    rows2 = np.array(rows2, np.int64)
+    _say(f"prefill case 2, {lq} queries over {L} keys, 32/8 heads")
+    o2, ref2, _ = _prefill_case(dev, [lq], [L], 32, 8, seed=L + 1, paged=True, rows=rows2)
+    check_attn(f64(o2)[rows2[:, 0], rows2[:, 1]], ref2, "prefill longest context, paged")
 
 
 def test_prefill_long_paged_chunk(dev):
