@@ -20,7 +20,8 @@
 //     B operand of the PV product.
 //   * A workgroup owns one kv head and the query heads of its GQA group that
 //     share it; each wave computes 32 query rows of one head.  For batches of
-//     long sequences (mean query length >= 2048) the workgroup has 8 waves
+//     long sequences (mean query length >= 2048), and for prefix hits of 1024+
+//     queries on average with 4 heads a workgroup, the workgroup has 8 waves
 //     (4 heads x 64 positions, or 2 x 128) and 128-key tiles, so each K/V tile
 //     staged in LDS feeds 256 query rows; otherwise 4 waves and 64-key tiles
 //     (more, smaller workgroups).  K and V are both kept row-major in LDS; the
