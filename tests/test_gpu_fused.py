@@ -164,3 +164,22 @@ def test_fused_odd_head_counts_and_token_counts(dev, table_dev, table_host, hq, 
     if n > 2:
         slots[2] = nb * 256          # a slot past the pool: skipped like -1
     _fused_case(dev, table_dev, table_host, s, qkv, gq, gk, pos, slots, nb, seed=hq + n)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_fused_random_shapes(dev, table_dev, table_host, case):
+    """Seeded random head counts (kv heads 1-8, groups 1-8), token counts (log-uniform up to
+    4000), input scales, positions over the whole table and slot maps with padding."""
+    rng = wl.rng_for(96, case, 0)
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    hq = hkv * int(rng.integers(1, 9))
+    n = int(np.exp(rng.uniform(0, np.log(4001))))
+    s = wl.Shape(num_q_heads=hq, num_kv_heads=hkv)
+    _say(f"qk_norm_rope_store random case {case}: {hq}/{hkv} heads, {n} tokens")
+    qkv = wl.normal_bf16(rng, (n, s.qkv_width), scale=float(rng.choice([0.25, 2.0, 16.0])))
+    gq, gk = wl.gamma_bf16(rng), wl.gamma_bf16(rng)
+    pos = rng.integers(0, 40960, size=n).astype(np.int64)
+    nb = (n + 255) // 256 + int(rng.integers(1, 4))
+    slots = rng.permutation(nb * 256)[:n].astype(np.int32)
+    slots[rng.random(n) < 0.05] = -1
+    _fused_case(dev, table_dev, table_host, s, qkv, gq, gk, pos, slots, nb, seed=900 + case)

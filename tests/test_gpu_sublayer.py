@@ -67,6 +67,26 @@ def test_add_rms_norm_matches_oracle(dev, n_tokens, hidden):
     _check_rms(bits(y0), ref_y0, normed0, g, "y (no residual)")
 
 
+@pytest.mark.parametrize("case", range(8))
+def test_add_rms_norm_random_shapes(dev, case):
+    """Seeded random token counts (log-uniform up to 5000) and widths (multiples of 8 up to
+    16384, every lane-count and chunk-count path of the kernel), with and without a residual."""
+    rng = wl.rng_for(90, case, 0)
+    hidden = 8 * int(rng.integers(1, 2049))
+    t = min(int(np.exp(rng.uniform(0, np.log(5001)))), 4_000_000 // hidden)
+    _say(f"add_rms_norm random case {case}: T={t} hidden={hidden}")
+    x, r, g = wl.add_rms_inputs(1000 + case, t, hidden)
+    xd, rd, gd = to_dev(x, dev), to_dev(r, dev), to_dev(g, dev)
+    y, res = pkv.add_rms_norm(xd, rd, gd, 1e-6)
+    y0, _ = pkv.add_rms_norm(xd, None, gd, 1e-6)
+    torch.cuda.synchronize()
+    ref_y, ref_res, normed = sl.add_rms_norm(x, r, g, 1e-6)
+    assert np.array_equal(bits(res), ref_res), "new residual must be bit-exact"
+    _check_rms(bits(y), ref_y, normed, g, "y")
+    ref_y0, _, normed0 = sl.add_rms_norm(x, None, g, 1e-6)
+    _check_rms(bits(y0), ref_y0, normed0, g, "y (no residual)")
+
+
 def test_add_rms_norm_in_place(dev):
     _say("add_rms_norm in place")
     x, r, g = wl.add_rms_inputs(3, 300, 4096)
@@ -90,6 +110,24 @@ def test_silu_and_mul_matches_oracle(dev, n_tokens, inter):
     got_bits = bits(out)
     got = wl.bf16_to_f32(got_bits).astype(np.float64)
     # fp32 evaluation (exp, divide, multiply: a few 2^-24 relative) then one rounding
+    bad = np.abs(got - ref) > bf16_ulp(ref)
+    assert not bad.any(), f"{bad.sum()} values beyond one bf16 ulp"
+    assert np.mean(got_bits == ref_bits) >= 0.99
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_silu_and_mul_random_shapes(dev, case):
+    """Seeded random token counts and intermediate widths (multiples of 8 up to 24576)."""
+    rng = wl.rng_for(91, case, 0)
+    inter = 8 * int(rng.integers(1, 3073))
+    t = min(int(np.exp(rng.uniform(0, np.log(3001)))), 2_000_000 // inter)
+    _say(f"silu_and_mul random case {case}: T={t} I={inter}")
+    x = wl.silu_inputs(2000 + case, t, inter)
+    out = pkv.silu_and_mul(to_dev(x, dev))
+    torch.cuda.synchronize()
+    ref, ref_bits = sl.silu_and_mul(x)
+    got_bits = bits(out)
+    got = wl.bf16_to_f32(got_bits).astype(np.float64)
     bad = np.abs(got - ref) > bf16_ulp(ref)
     assert not bad.any(), f"{bad.sum()} values beyond one bf16 ulp"
     assert np.mean(got_bits == ref_bits) >= 0.99
