@@ -21,7 +21,10 @@
 //     sort), and workgroups take them largest first: with contexts of very
 //     different lengths the last workgroups to start are the smallest, so the
 //     tail stays short.  A grid that fits the chip at once skips the sort.
-//   * Loads run one 16-key chunk ahead in a register ring.
+//   * Loads run one 16-key chunk ahead in a register ring.  K and V are read
+//     with non-temporal loads: each byte is read once, so keeping it in the
+//     caches only displaces other lines (8B batch 1782 -> 1718 us, 0.6B batch
+//     197 -> 182 us, outputs unchanged).
 //   * Both products on MFMA.  Scores: v_mfma_f32_16x16x32_bf16 with A = 16 keys
 //     x 32 dims straight from global memory and B = the group's q vectors
 //     (columns >= G are zero); a lane then holds 4 keys of one head column.
@@ -341,12 +344,12 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
         // K as the A operand: key col, dims 8*grp + 32*st
         const uint16_t* kp = k_cache + (r0 + col) * row + (int64_t)g * kHeadDim + 8 * grp;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) c.k[st] = ldg128(kp + 32 * st);
+        for (int st = 0; st < 4; ++st) c.k[st] = ldg128_stream(kp + 32 * st);
         __builtin_amdgcn_sched_barrier(0);   // K before V: the scores wait only for K
         // V rows: key grp + 4*i, dims 8*col .. +7 (staged through LDS for the transposed read)
         const uint16_t* vp = v_cache + (r0 + grp) * row + (int64_t)g * kHeadDim + 8 * col;
 #pragma unroll
-        for (int i = 0; i < kCK / 4; ++i) c.v[i] = ldg128(vp + (int64_t)(4 * i) * row);
+        for (int i = 0; i < kCK / 4; ++i) c.v[i] = ldg128_stream(vp + (int64_t)(4 * i) * row);
     };
 
     float m_ref = -INFINITY;          // lazy reference max of column col (log2 units)

@@ -31,6 +31,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ u32x4 ldg128(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void stg128(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+// Data read or written once, larger than the caches: non-temporal accesses stream
+// it through without displacing what other accesses reuse.
+__device__ __forceinline__ u32x4 ldg128_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void stg128_stream(void* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -16,7 +16,13 @@
 // not once per head.  The sum
 // of squares is a 16-lane butterfly; the rotation partner of elements
 // [8s, 8s+8) lives in lane s ^ 8, fetched with a cross-lane shuffle.  Math is
-// fp32 throughout and the result is rounded to bf16 once.
+// fp32 throughout and the result is rounded to bf16 once.  The q/k/v rows are
+// read, and k'/v written into the cache, with non-temporal accesses (each byte
+// is touched once); the table rows and weights, which every token reads, go
+// through the caches as usual.  The fused pass writes q' through the caches
+// too (32768 tokens at 32/8 heads: 146 -> 131 us; streaming q' as well: 149 us).
+// The unfused pass streams q' and k' (its outputs' dirty lines otherwise slow the
+// store_kvcache that follows: 114 + 66 us against 118 + 47 us for the pair).
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -167,16 +173,16 @@ __global__ void __launch_bounds__(256) qk_norm_rope_kernel(
         const uint16_t* qt = q + t * q_row_stride + sub * 8;
         uint16_t* qo = q_out + t * hq * kHeadDim + sub * 8;
         norm_rope_heads(lo, min(hi, hq), grp, sub, ldg128(gq + sub * 8), ldg128(gq + (sub ^ 8) * 8), eps, cv, sv,
-                        [&](int h) { return ldg128(qt + (int64_t)h * kHeadDim); },
-                        [&](int h, u32x4 r) { stg128(qo + (int64_t)h * kHeadDim, r); });
+                        [&](int h) { return ldg128_stream(qt + (int64_t)h * kHeadDim); },
+                        [&](int h, u32x4 r) { stg128_stream(qo + (int64_t)h * kHeadDim, r); });
     }
     if (hi > hq) {
         const uint16_t* kt = k + t * k_row_stride + sub * 8;
         uint16_t* ko = k_out + t * hkv * kHeadDim + sub * 8;
         norm_rope_heads(max(lo, hq) - hq, min(hi, hq + hkv) - hq, grp, sub, ldg128(gk + sub * 8),
                         ldg128(gk + (sub ^ 8) * 8), eps, cv, sv,
-                        [&](int h) { return ldg128(kt + (int64_t)h * kHeadDim); },
-                        [&](int h, u32x4 r) { stg128(ko + (int64_t)h * kHeadDim, r); });
+                        [&](int h) { return ldg128_stream(kt + (int64_t)h * kHeadDim); },
+                        [&](int h, u32x4 r) { stg128_stream(ko + (int64_t)h * kHeadDim, r); });
     }
 }
 
@@ -212,12 +218,12 @@ __global__ void __launch_bounds__(256) qk_norm_rope_store_kernel(
 #pragma unroll
             for (int c = 0; c < kChunk; ++c) {
                 const int h = h0 + 4 * c + grp;
-                if (h < vhi) x[c] = ldg128(vt + (int64_t)h * kHeadDim);
+                if (h < vhi) x[c] = ldg128_stream(vt + (int64_t)h * kHeadDim);
             }
 #pragma unroll
             for (int c = 0; c < kChunk; ++c) {
                 const int h = h0 + 4 * c + grp;
-                if (h < vhi) stg128(vc + (int64_t)h * kHeadDim, x[c]);
+                if (h < vhi) stg128_stream(vc + (int64_t)h * kHeadDim, x[c]);
             }
         }
     }
@@ -228,7 +234,7 @@ __global__ void __launch_bounds__(256) qk_norm_rope_store_kernel(
         const uint16_t* qt = q + t * q_row_stride + sub * 8;
         uint16_t* qo = q_out + t * hq * kHeadDim + sub * 8;
         norm_rope_heads(lo, min(hi, hq), grp, sub, ldg128(gq + sub * 8), ldg128(gq + (sub ^ 8) * 8), eps, cv, sv,
-                        [&](int h) { return ldg128(qt + (int64_t)h * kHeadDim); },
+                        [&](int h) { return ldg128_stream(qt + (int64_t)h * kHeadDim); },
                         [&](int h, u32x4 r) { stg128(qo + (int64_t)h * kHeadDim, r); });
     }
     if (hi > hq) {
@@ -236,10 +242,10 @@ __global__ void __launch_bounds__(256) qk_norm_rope_store_kernel(
         uint16_t* ko = k_out ? k_out + t * hkv * kHeadDim + sub * 8 : nullptr;
         norm_rope_heads(max(lo, hq) - hq, min(hi, hq + hkv) - hq, grp, sub, ldg128(gk + sub * 8),
                         ldg128(gk + (sub ^ 8) * 8), eps, cv, sv,
-                        [&](int h) { return ldg128(kt + (int64_t)h * kHeadDim); },
+                        [&](int h) { return ldg128_stream(kt + (int64_t)h * kHeadDim); },
                         [&](int h, u32x4 r) {
                             if (ko) stg128(ko + (int64_t)h * kHeadDim, r);
-                            if (kc) stg128(kc + (int64_t)h * kHeadDim, r);
+                            if (kc) stg128_stream(kc + (int64_t)h * kHeadDim, r);
                         });
     }
 }

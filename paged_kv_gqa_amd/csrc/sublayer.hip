@@ -29,7 +29,9 @@ namespace {
 // A row of `hidden` elements is covered by `lpr` lanes (64, 128 or 256; 256 /
 // lpr rows per 256-thread block), each owning up to NC chunks of 8 elements
 // strided by lpr chunks.  The row's sum of squares: a wave butterfly, then the
-// row's waves combine through LDS in wave order (deterministic).
+// row's waves combine through LDS in wave order (deterministic).  x, residual and
+// both outputs stream through the caches (non-temporal: 192 -> 181 us on
+// [32768, 4096]); gamma, which every row reads, is cached as usual.
 template <int NC>
 __global__ void __launch_bounds__(256) add_rms_norm_kernel(const uint16_t* x, const uint16_t* residual,
                                                            const uint16_t* __restrict__ gamma, uint16_t* y,
@@ -50,9 +52,9 @@ __global__ void __launch_bounds__(256) add_rms_norm_kernel(const uint16_t* x, co
     for (int k = 0; k < NC; ++k) {
         const int c = li + k * lpr;
         const bool ok = live && c < chunks;
-        const u32x4 xv = ok ? ldg128(x + base + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 xv = ok ? ldg128_stream(x + base + 8 * c) : u32x4{0u, 0u, 0u, 0u};
         if (residual) {
-            const u32x4 rv = ok ? ldg128(residual + base + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+            const u32x4 rv = ok ? ldg128_stream(residual + base + 8 * c) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 // fp32 add of the two bf16 values (exact inputs, one IEEE rounding)
@@ -74,7 +76,7 @@ __global__ void __launch_bounds__(256) add_rms_norm_kernel(const uint16_t* x, co
             u32x4 ro;
 #pragma unroll
             for (int w = 0; w < 4; ++w) ro[w] = pack_bf16x2(s[k][2 * w], s[k][2 * w + 1]);
-            stg128(residual_out + base + 8 * c, ro);
+            stg128_stream(residual_out + base + 8 * c, ro);
         }
     }
     ss = wave_sum(ss);
@@ -98,7 +100,7 @@ __global__ void __launch_bounds__(256) add_rms_norm_kernel(const uint16_t* x, co
             const float n1 = bf16lo(pack_bf16x2(s[k][2 * w + 1] * r, 0.f));
             out[w] = pack_bf16x2(n0 * bf16lo(gv[w]), n1 * bf16hi(gv[w]));
         }
-        stg128(y + base + 8 * c, out);
+        stg128_stream(y + base + 8 * c, out);
     }
 }
 
@@ -106,7 +108,22 @@ __global__ void __launch_bounds__(256) add_rms_norm_kernel(const uint16_t* x, co
 // SiluAndMul
 // ---------------------------------------------------------------------------
 // One lane per 8 output elements: the gate chunk and the up chunk of the same
-// columns, silu(g) * u in fp32, one rounding.
+// columns, silu(g) * u in fp32, one rounding.  A lane loads two chunks' gate and
+// up halves before computing either, and rows stream through the caches with
+// non-temporal loads and stores (together 7% faster on [32768, 2 x 12288]; the
+// non-temporal accesses alone, or the paired loads alone, gain under 1.5%).
+__device__ __forceinline__ u32x4 silu_mul8(u32x4 gv, u32x4 uv) {
+    u32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float g0 = bf16lo(gv[w]), g1 = bf16hi(gv[w]);
+        const float a0 = g0 / (1.0f + __expf(-g0)) * bf16lo(uv[w]);
+        const float a1 = g1 / (1.0f + __expf(-g1)) * bf16hi(uv[w]);
+        o[w] = pack_bf16x2(a0, a1);
+    }
+    return o;
+}
+
 __global__ void __launch_bounds__(256) silu_and_mul_kernel(const uint16_t* __restrict__ x, int64_t x_row_stride,
                                                            uint16_t* __restrict__ out, int64_t out_row_stride,
                                                            int32_t n_tokens, int32_t inter) {
@@ -114,19 +131,15 @@ __global__ void __launch_bounds__(256) silu_and_mul_kernel(const uint16_t* __res
     for (int64_t t = blockIdx.x; t < n_tokens; t += gridDim.x) {
         const uint16_t* row = x + t * x_row_stride;
         uint16_t* orow = out + t * out_row_stride;
-        for (int c = threadIdx.x; c < cpr; c += blockDim.x) {
-            const u32x4 gv = ldg128(row + 8 * c);
-            const u32x4 uv = ldg128(row + inter + 8 * c);
-            u32x4 o;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float g0 = bf16lo(gv[w]), g1 = bf16hi(gv[w]);
-                const float a0 = g0 / (1.0f + __expf(-g0)) * bf16lo(uv[w]);
-                const float a1 = g1 / (1.0f + __expf(-g1)) * bf16hi(uv[w]);
-                o[w] = pack_bf16x2(a0, a1);
-            }
-            stg128(orow + 8 * c, o);
+        const int step = (int)blockDim.x;
+        int c = threadIdx.x;
+        for (; c + step < cpr; c += 2 * step) {
+            const u32x4 gv0 = ldg128_stream(row + 8 * c), uv0 = ldg128_stream(row + inter + 8 * c);
+            const u32x4 gv1 = ldg128_stream(row + 8 * (c + step)), uv1 = ldg128_stream(row + inter + 8 * (c + step));
+            stg128_stream(orow + 8 * c, silu_mul8(gv0, uv0));
+            stg128_stream(orow + 8 * (c + step), silu_mul8(gv1, uv1));
         }
+        if (c < cpr) stg128_stream(orow + 8 * c, silu_mul8(ldg128_stream(row + 8 * c), ldg128_stream(row + inter + 8 * c)));
     }
 }
 
