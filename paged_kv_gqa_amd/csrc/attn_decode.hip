@@ -21,10 +21,13 @@
 //     sort), and workgroups take them largest first: with contexts of very
 //     different lengths the last workgroups to start are the smallest, so the
 //     tail stays short.  A grid that fits the chip at once skips the sort.
-//   * Loads run one 16-key chunk ahead in a register ring.  K and V are read
-//     with non-temporal loads: each byte is read once, so keeping it in the
-//     caches only displaces other lines (8B batch 1782 -> 1718 us, 0.6B batch
-//     197 -> 182 us, outputs unchanged).
+//   * Loads run one 16-key chunk ahead in a register ring.  V is read with
+//     non-temporal loads: each V load instruction consumes whole cache lines
+//     that nothing reads again, so keeping them only displaces other lines.  K
+//     goes through the caches as usual: a K line is consumed by two load
+//     instructions (dims 0-63 and 64-127 of a row), and streaming it made the
+//     second miss.  8B batch 1782 -> 1634 us, 0.6B batch 197 -> 179 us (both
+//     streamed: 1718 and 182 us), outputs unchanged.
 //   * Both products on MFMA.  Scores: v_mfma_f32_16x16x32_bf16 with A = 16 keys
 //     x 32 dims straight from global memory and B = the group's q vectors
 //     (columns >= G are zero); a lane then holds 4 keys of one head column.
@@ -344,7 +347,7 @@ __global__ void __launch_bounds__(kDecThreads, kOcc) decode_split_kernel(
         // K as the A operand: key col, dims 8*grp + 32*st
         const uint16_t* kp = k_cache + (r0 + col) * row + (int64_t)g * kHeadDim + 8 * grp;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) c.k[st] = ldg128_stream(kp + 32 * st);
+        for (int st = 0; st < 4; ++st) c.k[st] = ldg128(kp + 32 * st);
         __builtin_amdgcn_sched_barrier(0);   // K before V: the scores wait only for K
         // V rows: key grp + 4*i, dims 8*col .. +7 (staged through LDS for the transposed read)
         const uint16_t* vp = v_cache + (r0 + grp) * row + (int64_t)g * kHeadDim + 8 * col;
