@@ -713,6 +713,28 @@ def test_decode_large_batch_short_contexts(dev):
     assert np.all(got[~live] == 0.0)
 
 
+def test_decode_8192_sequences(dev):
+    """8192 sequences of 0-64 tokens over a 64-block pool that they share at random (valid, as a
+    shared prefix is): the size sort over 8192 split items (16384 workgroups), one-split merges
+    and empty rows, every row against the oracle."""
+    rng = wl.rng_for(97, 1, 0)
+    B, nb = 8192, 64
+    ctx = rng.integers(0, 65, size=B).astype(np.int32)
+    ctx[:4] = [0, 1, 64, 63]
+    bt = np.stack([rng.integers(0, nb, size=B), np.full(B, -1)], 1).astype(np.int32)
+    kc = wl.normal_bf16(rng, (nb, 256, 8, D))
+    vc = wl.normal_bf16(rng, (nb, 256, 8, D))
+    q = wl.normal_bf16(rng, (B, 32, D))
+    _say("decode 8192 sequences, contexts 0..64 in a shared 64-block pool, 32/8 heads")
+    o = pkv.attn_decode_paged(to_dev(q, dev), to_dev(kc, dev), to_dev(vc, dev), to_dev(ctx, dev), to_dev(bt, dev))
+    torch.cuda.synchronize()
+    got = f64(o)
+    live = ctx > 0
+    ref = oracle.attn_decode(q[live], kc.reshape(-1, 8, D), vc.reshape(-1, 8, D), ctx[live], bt[live], 32, 8)
+    check_attn(got[live], ref, "decode 8192 sequences")
+    assert np.all(got[~live] == 0.0)
+
+
 def test_prefill_longest_context(dev):
     """One sequence of Qwen3's longest context (40960 tokens) at 32/8 heads, fresh, then its last
     2048 tokens as new queries over the paged cache; rows at both ends, at tile and 2^15
