@@ -713,6 +713,23 @@ def test_decode_large_batch_short_contexts(dev):
     assert np.all(got[~live] == 0.0)
 
 
+def test_prefill_2048_short_sequences(dev):
+    """2048 sequences of 0-16 new tokens at 32/8 heads (many one-block units, empty sequences
+    between them), then 512 of them over paged prefixes of up to 300 keys; every row against
+    the oracle."""
+    rng = wl.rng_for(93, 2, 0)
+    lq = [int(x) for x in rng.integers(0, 17, size=2048)]
+    lq[:3] = [0, 1, 16]
+    _say("prefill case 1, 2048 sequences of 0-16 tokens, 32/8 heads")
+    o, ref, _ = _prefill_case(dev, lq, lq, 32, 8, seed=2048)
+    check_attn(f64(o), ref, "prefill 2048 short sequences")
+    lq2 = lq[:512]                   # one 256-token block per sequence in the paged pool
+    lk = [q + int(p) for q, p in zip(lq2, rng.integers(0, 301, size=512))]
+    _say("prefill case 2, 512 sequences of 0-16 tokens over up to 316 keys, 32/8 heads")
+    o2, ref2, _ = _prefill_case(dev, lq2, lk, 32, 8, seed=2049, paged=True)
+    check_attn(f64(o2), ref2, "prefill 2048 short sequences, paged")
+
+
 def test_decode_8192_sequences(dev):
     """8192 sequences of 0-64 tokens over a 64-block pool that they share at random (valid, as a
     shared prefix is): the size sort over 8192 split items (16384 workgroups), one-split merges
